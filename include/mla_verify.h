@@ -1,0 +1,222 @@
+/*
+ * mla_verify.h - C ABI of libmla_verify.so: absorbed-MLA verify / sparse-decode
+ * attention for speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. A block of q_len draft-token queries per sequence, H heads
+ * each, every query a 576-element absorbed vector (512 latent + 64 rope),
+ * attends over the sequence's latent KV cache: one 576-element row per cached
+ * token, shared by all heads, whose first 512 elements are also the value.
+ * ("How a CUDA Kernel Designer Discovered That GPU Utilization Trumps Memory
+ * Bandwidth": sections "Context: The Problem and the Stakes" for verify
+ * attention and "The Warp-Per-Key Dot Product" for the 576-element score;
+ * "The Occupancy Probe", section "The Scene", for the 512-wide latent
+ * accumulator and the fp8 sparse decode.) For sequence b, query i, head h:
+ *
+ *   s_j   = sm_scale * <q[b,i,h,0:576], k_j[0:576]>      for visible j
+ *   lse   = ln sum_j exp(s_j)                           (natural log)
+ *   out[c]= sum_j exp(s_j - lse) * k_j[c]               for c < 512
+ *
+ * Visible positions (N = seq_lens[b]):
+ *   MLA_MASK_NONE   all N positions.
+ *   MLA_MASK_CAUSAL prefix P = N - q_len positions, plus drafts 0..i
+ *                   (draft d sits at position P + d).
+ *   MLA_MASK_TREE   prefix, plus draft d iff bit d of tree_anc[b,i] is set
+ *                   (ancestor-or-self mask, built by mla_build_tree_mask).
+ *   MLA_MASK_TOPK   exactly the positions topk_idx[b,i,0:topk] (prefix
+ *                   positions, distinct), fp8 cache only.
+ * An empty visible set yields out = 0 and lse = -inf.
+ *
+ * The KV axis of each sequence is cut into nsplit contiguous chunks of
+ * ceil(N / nsplit) positions ("How One Environment Variable Unlocked 3x
+ * Throughput", section "The Occupancy Revelation": the split count NSPLIT
+ * multiplies the grid); each chunk produces a normalised partial output and
+ * its LSE, and a second kernel merges them by log-sum-exp weights. The merge
+ * is exact in real arithmetic, so results do not depend on nsplit beyond
+ * floating-point rounding.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller (e.g. torch
+ *    tensors). The library never copies them, never frees them and never
+ *    keeps them after the call returns.
+ *  - Tensors are dense and row-major in the shapes given below.
+ *  - 16-byte alignment is required for q, the cache arrays and out (the
+ *    kernels use 16-byte vector loads and stores); 8 bytes for tree_anc;
+ *    4 bytes for the int32 arrays, lse and scale. Misalignment returns
+ *    MLA_ERR_ALIGN.
+ *  - Work is enqueued on `stream` and the call returns without waiting. All
+ *    argument checks happen on the host before any HIP call, so a bad
+ *    argument never launches anything.
+ *  - Errors are returned as negative MLA_ERR_* codes; nothing throws across
+ *    the ABI. Conditions only the GPU can see (a slot outside the pool, a
+ *    seq_len outside [q_len, slot_stride], a bad tree parent) set a sticky
+ *    per-device flag read by mla_get_device_error(); the offending key is
+ *    treated as masked and the kernels never read outside the pool.
+ */
+#ifndef MLA_VERIFY_H
+#define MLA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_VERIFY_ABI_VERSION 1
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1)  /* null pointer, bad size, bad enum, bad parent */
+#define MLA_ERR_ALIGN (-2)        /* pointer not aligned as required */
+#define MLA_ERR_UNSUPPORTED (-3)  /* shape or combination outside what the kernels cover */
+#define MLA_ERR_WORKSPACE (-4)    /* workspace must grow while the stream is being captured */
+#define MLA_ERR_LAUNCH (-5)       /* a HIP call or kernel launch failed */
+
+/* Device-side error flag bits (mla_get_device_error). */
+#define MLA_DEVERR_SLOT_RANGE 0x1u   /* slot_table entry outside [0, pool_rows) */
+#define MLA_DEVERR_SEQ_LEN 0x2u      /* seq_len < q_len (masked kinds) or > slot_stride */
+#define MLA_DEVERR_TREE_PARENT 0x4u  /* parent outside [-1, i-1] in mla_build_tree_mask */
+#define MLA_DEVERR_TOPK_RANGE 0x8u   /* top-k position outside [0, seq_len) */
+
+/* Cache element types. */
+#define MLA_KV_BF16 0      /* latent: bf16 [pool_rows, 576] (512 latent ++ 64 rope) */
+#define MLA_KV_FP8_E4M3 1  /* latent: OCP E4M3FN [pool_rows, 512]; rope: bf16 [pool_rows, 64];
+                              scale: fp32 [pool_rows] multiplying the latent part */
+
+/* Mask kinds (see the header comment for the visible sets). */
+#define MLA_MASK_NONE 0
+#define MLA_MASK_CAUSAL 1
+#define MLA_MASK_TREE 2
+#define MLA_MASK_TOPK 3
+
+/* Limits. */
+#define MLA_MAX_Q_LEN 64     /* draft masks are 64-bit */
+#define MLA_MAX_HEADS 128
+#define MLA_MAX_NSPLIT 1024
+#define MLA_MAX_TOPK 65536
+
+/* Queries: bf16 [batch, q_len, heads, 576], absorbed (512 latent ++ 64 rope). */
+typedef struct mla_q_t {
+  const void* data;
+  int batch;
+  int q_len;
+  int heads;
+  float sm_scale; /* multiplies the full 576-element dot product; > 0 and finite */
+} mla_q_t;
+
+/* Latent KV cache with page_size = 1: one pool row per cached token. */
+typedef struct mla_kv_t {
+  int dtype;            /* MLA_KV_BF16 or MLA_KV_FP8_E4M3 */
+  const void* latent;   /* see MLA_KV_* */
+  const void* rope;     /* NULL for bf16; bf16 [pool_rows, 64] for fp8 */
+  const float* scale;   /* NULL for bf16; fp32 [pool_rows] for fp8 */
+  int64_t pool_rows;    /* number of rows in the pool */
+  int slot_stride;      /* row length of slot_table (max tokens per sequence) */
+  int max_seq_len;      /* host-side upper bound of seq_lens used to size the
+                           split grid; 0 means slot_stride */
+} mla_kv_t;
+
+typedef struct mla_mask_t {
+  int kind;                  /* MLA_MASK_* */
+  const uint64_t* tree_anc;  /* MLA_MASK_TREE: device uint64 [batch, q_len] */
+  const int32_t* topk_idx;   /* MLA_MASK_TOPK: device int32 [batch, q_len, topk] */
+  int topk;                  /* MLA_MASK_TOPK: entries per (sequence, query) */
+} mla_mask_t;
+
+/* Plan of one call, as chosen by the library (for tests and measurement). */
+typedef struct mla_plan_t {
+  int nsplit;            /* KV splits per sequence actually used */
+  int waves_per_group;   /* wavefronts (16 query rows each) per workgroup */
+  int row_groups;        /* workgroups along the query-row axis per split */
+  int grid;              /* split-kernel workgroups */
+  size_t workspace_bytes;/* partial storage needed (0 when nsplit == 1) */
+  int kernel;            /* 0 = bf16 verify, 1 = fp8 top-k sparse */
+} mla_plan_t;
+
+/*
+ * Verify / sparse-decode attention.
+ *   slot_table: int32 [batch, slot_stride]; position j of sequence b lives in
+ *               pool row slot_table[b, j] (page_size = 1).
+ *   seq_lens:   int32 [batch]; N_b. For CAUSAL/TREE this counts the prefix
+ *               plus the q_len drafts, whose rows are already in the cache
+ *               at positions N_b - q_len .. N_b - 1. For TOPK it is the
+ *               prefix length bounding the top-k positions.
+ *   out:        fp32 [batch, q_len, heads, 512].
+ *   lse:        fp32 [batch, q_len, heads] or NULL.
+ *   nsplit:     KV splits per sequence; <= 0 picks one from the CU count
+ *               (mla_choose_nsplit). Capped at MLA_MAX_NSPLIT.
+ * When nsplit > 1 the call uses the library's workspace for (device,
+ * stream): it grows on demand (synchronising `stream` first), or returns
+ * MLA_ERR_WORKSPACE if the stream is capturing and the reserve is too small.
+ * Calls on the same stream are ordered; calls on different streams have
+ * separate workspaces.
+ */
+int mla_verify_attn(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table,
+                    const int32_t* seq_lens, const mla_mask_t* mask_desc, float* out, float* lse,
+                    int nsplit, hipStream_t stream);
+
+/* The two halves of mla_verify_attn with identical arguments: the split
+ * kernel alone (writes partials to the workspace, or out/lse directly when
+ * the plan has nsplit == 1), then the merge alone (no-op when nsplit == 1).
+ * Calling mla_verify_split then mla_verify_combine on one stream equals one
+ * mla_verify_attn. Exposed so a caller can time or schedule the kernels
+ * separately. */
+int mla_verify_split(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table,
+                     const int32_t* seq_lens, const mla_mask_t* mask_desc, float* out, float* lse,
+                     int nsplit, hipStream_t stream);
+int mla_verify_combine(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table,
+                       const int32_t* seq_lens, const mla_mask_t* mask_desc, float* out, float* lse,
+                       int nsplit, hipStream_t stream);
+
+/* Fill *plan for a call with these arguments (host only, no HIP call except
+ * reading the current device's CU count once). Returns a status code. */
+int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_desc, int nsplit,
+             mla_plan_t* plan);
+
+/* Split count the library picks when nsplit <= 0: a pure function of the
+ * shape and the CU count, so it is deterministic and safe under graph
+ * capture. ("How One Environment Variable Unlocked 3x Throughput", section
+ * "The Occupancy Revelation": a small per-rank head count shrinks the grid
+ * until the machine starves, and more splits refill it.) */
+int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus);
+
+/* Bytes of split partials one call needs: batch * nsplit * q_len * heads *
+ * (512 + 1) * 4, or 0 for nsplit <= 1. */
+size_t mla_workspace_bytes(int batch, int q_len, int heads, int nsplit);
+
+/* Make the workspace of (current device, stream) at least `bytes` long and
+ * allocate the device error flag, so later calls (e.g. under graph capture)
+ * do not allocate. Synchronises `stream` if it has to reallocate. */
+int mla_reserve_workspace(size_t bytes, hipStream_t stream);
+
+/* Draft tree -> ancestor-or-self masks. parents: int32 [batch, q_len] with
+ * parents[b,i] in [-1, i-1] (-1 = child of the prefix tail). Bit d of
+ * anc_out[b,i] is set iff draft d is node i or one of its ancestors.
+ * ("How One Environment Variable Unlocked 3x Throughput", sections "The
+ * Broader Context" and "Input Knowledge Required": the draft tree is built
+ * per step and turned into the verify mask.)
+ * Device variant: pointers are device memory, enqueued on `stream`; a bad
+ * parent sets MLA_DEVERR_TREE_PARENT and yields mask 1<<i for that node.
+ * Host variant: pointers are host memory; a bad parent returns
+ * MLA_ERR_INVALID_ARG. q_len must be in [1, 64]. */
+int mla_build_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* anc_out,
+                        hipStream_t stream);
+int mla_build_tree_mask_host(const int32_t* parents, int batch, int q_len, uint64_t* anc_out);
+
+/* Read (and optionally clear) the current device's sticky error flags.
+ * Synchronises the device. Returns the MLA_DEVERR_* bits, or a negative
+ * status code. */
+int mla_get_device_error(int clear);
+
+/* Text for a status code (static storage). */
+const char* mla_status_string(int status);
+
+/* MLA_VERIFY_ABI_VERSION of the built library. */
+int mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H */

@@ -1,0 +1,378 @@
+// C-ABI host layer of libmla_verify.so: argument validation, planning
+// (row grouping and split count), per-(device, stream) workspace, device
+// error flag, and kernel launches. Validation runs before any HIP call.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "mla_internal.h"
+#include "mla_verify.h"
+
+namespace {
+
+using mla::kDk;
+using mla::kDv;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ----------------------------------------------------------------- per-device state
+struct WsKey {
+  int device;
+  hipStream_t stream;
+  bool operator<(const WsKey& o) const {
+    return device != o.device ? device < o.device : reinterpret_cast<uintptr_t>(stream) < reinterpret_cast<uintptr_t>(o.stream);
+  }
+};
+struct WsBuf {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<WsKey, WsBuf> g_ws;
+std::map<int, unsigned*> g_err;
+std::map<int, int> g_cus;
+
+int current_device(int* dev) {
+  return hipGetDevice(dev) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int device_cus(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  g_cus[dev] = cus;
+  return cus;
+}
+
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+// Per-device constant block (allocated and zeroed on first use): the sticky
+// error word at offset 0 and a zero cache row at kZeroRowOffset.
+constexpr size_t kDevBlockBytes = 4096;
+constexpr size_t kZeroRowOffset = 256;
+
+int error_word(int dev, hipStream_t stream, unsigned** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_err.find(dev);
+  if (it != g_err.end()) {
+    *out = it->second;
+    return MLA_OK;
+  }
+  if (stream && stream_capturing(stream)) return MLA_ERR_WORKSPACE;
+  unsigned* p = nullptr;
+  if (hipMalloc(&p, kDevBlockBytes) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (hipMemset(p, 0, kDevBlockBytes) != hipSuccess) return MLA_ERR_LAUNCH;
+  g_err[dev] = p;
+  *out = p;
+  return MLA_OK;
+}
+
+int workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  WsBuf& w = g_ws[WsKey{dev, stream}];
+  if (w.bytes >= bytes) {
+    *out = w.ptr;
+    return MLA_OK;
+  }
+  if (stream_capturing(stream)) return MLA_ERR_WORKSPACE;
+  if (w.ptr) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_LAUNCH;
+    if (hipFree(w.ptr) != hipSuccess) return MLA_ERR_LAUNCH;
+    w.ptr = nullptr;
+    w.bytes = 0;
+  }
+  // round up to 2 MiB so small growth steps do not reallocate every call
+  const size_t want = (bytes + (2u << 20) - 1) & ~((size_t)(2u << 20) - 1);
+  if (hipMalloc(&w.ptr, want) != hipSuccess) {
+    w.ptr = nullptr;
+    return MLA_ERR_LAUNCH;
+  }
+  w.bytes = want;
+  *out = w.ptr;
+  return MLA_OK;
+}
+
+// ----------------------------------------------------------------- planning
+// Query rows are cut into 16-row blocks (one wavefront each); a workgroup
+// takes `waves` blocks. Prefer no padding; then 4 or 8 waves (even SIMD load).
+void choose_row_groups(int rows, int* waves, int* groups) {
+  const int blocks = (rows + 15) / 16;
+  if (blocks <= 8) {
+    *waves = blocks;
+    *groups = 1;
+    return;
+  }
+  int best_w = 8, best_pad = 1 << 30;
+  const int order[] = {4, 8, 6, 5, 7};
+  for (int w : order) {
+    const int g = (blocks + w - 1) / w;
+    const int pad = g * w - blocks;
+    if (pad < best_pad) {
+      best_pad = pad;
+      best_w = w;
+    }
+  }
+  *waves = best_w;
+  *groups = (blocks + best_w - 1) / best_w;
+}
+
+int choose_nsplit_impl(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus) {
+  if (batch < 1 || q_len < 1 || heads < 1 || num_cus < 1) return 1;
+  int waves, groups;
+  choose_row_groups(q_len * heads, &waves, &groups);
+  const long wgs_per_split = (long)batch * groups;
+  // Aim at one workgroup per CU; never fewer than 4 tiles (128 keys) per split.
+  long s = (num_cus + wgs_per_split - 1) / wgs_per_split;
+  const long keys = kv_dtype == MLA_KV_FP8_E4M3 ? max_seq_len : max_seq_len;
+  const long cap = std::max<long>(1, (keys + 127) / 128);
+  s = std::min(s, cap);
+  s = std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
+  return (int)s;
+}
+
+struct Call {
+  mla::Args a;
+  int waves = 1, groups = 1;
+  int kernel = 0;
+  size_t ws_bytes = 0;
+};
+
+int validate(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const int32_t* seq_lens,
+             const mla_mask_t* m, const float* out, const float* lse, int nsplit, bool need_data) {
+  if (!q || !kv || !m) return MLA_ERR_INVALID_ARG;
+  if (need_data && (!q->data || !slot_table || !seq_lens || !out || !kv->latent)) return MLA_ERR_INVALID_ARG;
+  if (q->batch < 1 || q->q_len < 1 || q->heads < 1) return MLA_ERR_INVALID_ARG;
+  if (q->q_len > MLA_MAX_Q_LEN || q->heads > MLA_MAX_HEADS) return MLA_ERR_UNSUPPORTED;
+  if (q->batch > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!(q->sm_scale > 0.f) || !std::isfinite(q->sm_scale)) return MLA_ERR_INVALID_ARG;
+  if (kv->pool_rows < 1 || kv->slot_stride < 1) return MLA_ERR_INVALID_ARG;
+  if (kv->max_seq_len < 0 || kv->max_seq_len > kv->slot_stride) return MLA_ERR_INVALID_ARG;
+  if (nsplit > MLA_MAX_NSPLIT) return MLA_ERR_INVALID_ARG;
+  if (kv->dtype == MLA_KV_BF16) {
+    if (m->kind != MLA_MASK_NONE && m->kind != MLA_MASK_CAUSAL && m->kind != MLA_MASK_TREE) {
+      return m->kind == MLA_MASK_TOPK ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+    }
+    if (m->kind == MLA_MASK_TREE) {
+      if (need_data && !m->tree_anc) return MLA_ERR_INVALID_ARG;
+      if (!aligned(m->tree_anc, 8)) return MLA_ERR_ALIGN;
+    }
+  } else if (kv->dtype == MLA_KV_FP8_E4M3) {
+    if (m->kind != MLA_MASK_TOPK) {
+      return (m->kind >= MLA_MASK_NONE && m->kind <= MLA_MASK_TREE) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+    }
+    if (need_data && (!kv->rope || !kv->scale || !m->topk_idx)) return MLA_ERR_INVALID_ARG;
+    if (m->topk < 1) return MLA_ERR_INVALID_ARG;
+    if (m->topk > MLA_MAX_TOPK) return MLA_ERR_UNSUPPORTED;
+    if (!aligned(kv->rope, 16) || !aligned(kv->scale, 4) || !aligned(m->topk_idx, 4)) return MLA_ERR_ALIGN;
+  } else {
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (!aligned(q->data, 16) || !aligned(kv->latent, 16) || !aligned(out, 16)) return MLA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(slot_table, 4) || !aligned(seq_lens, 4)) return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsplit, int num_cus, Call* c) {
+  const int rows = q->q_len * q->heads;
+  choose_row_groups(rows, &c->waves, &c->groups);
+  c->kernel = kv->dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
+  const int maxlen = kv->max_seq_len > 0 ? kv->max_seq_len : kv->slot_stride;
+  const int seqlen_for_split = c->kernel == 1 ? std::min(maxlen, m->topk) : maxlen;
+  int s = nsplit > 0 ? nsplit : choose_nsplit_impl(q->batch, q->q_len, q->heads, seqlen_for_split, kv->dtype, num_cus);
+  if (s > MLA_MAX_NSPLIT) return MLA_ERR_INVALID_ARG;
+  const long grid = (long)s * c->groups;
+  if (grid > 0x7fffffffL || c->groups > 65535) return MLA_ERR_UNSUPPORTED;
+  c->a.nsplit = s;
+  c->ws_bytes = mla_workspace_bytes(q->batch, q->q_len, q->heads, s);
+  return MLA_OK;
+}
+
+void fill_args(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const int32_t* seq_lens,
+               const mla_mask_t* m, float* out, float* lse, Call* c) {
+  mla::Args& a = c->a;
+  a.q = q->data;
+  a.latent = kv->latent;
+  a.rope = kv->rope;
+  a.kscale = kv->scale;
+  a.slots = slot_table;
+  a.seq_lens = seq_lens;
+  a.anc = m->kind == MLA_MASK_TREE ? m->tree_anc : nullptr;
+  a.topk_idx = m->kind == MLA_MASK_TOPK ? m->topk_idx : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  a.err = nullptr;
+  a.zero_row = nullptr;
+  a.pool_rows = kv->pool_rows;
+  a.slot_stride = kv->slot_stride;
+  a.batch = q->batch;
+  a.q_len = q->q_len;
+  a.heads = q->heads;
+  a.rows = q->q_len * q->heads;
+  a.mask_kind = m->kind;
+  a.topk = m->kind == MLA_MASK_TOPK ? m->topk : 0;
+  a.scale_log2 = (float)((double)q->sm_scale * 1.4426950408889634);
+}
+
+enum Stage { kSplit = 1, kCombine = 2, kBoth = 3 };
+
+int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const int32_t* seq_lens,
+        const mla_mask_t* m, float* out, float* lse, int nsplit, hipStream_t stream, int stages) {
+  int st = validate(q, kv, slot_table, seq_lens, m, out, lse, nsplit, true);
+  if (st != MLA_OK) return st;
+  int dev = 0;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  Call c;
+  fill_args(q, kv, slot_table, seq_lens, m, out, lse, &c);
+  if ((st = make_plan(q, kv, m, nsplit, device_cus(dev), &c)) != MLA_OK) return st;
+  if ((st = error_word(dev, stream, &c.a.err)) != MLA_OK) return st;
+  c.a.zero_row = reinterpret_cast<const char*>(c.a.err) + kZeroRowOffset;
+  if (c.a.nsplit > 1) {
+    void* ws = nullptr;
+    if ((st = workspace(dev, stream, c.ws_bytes, &ws)) != MLA_OK) return st;
+    const size_t n_o = (size_t)q->batch * c.a.nsplit * c.a.rows * kDv;
+    c.a.part_o = static_cast<float*>(ws);
+    c.a.part_lse = static_cast<float*>(ws) + n_o;
+  }
+  if (stages & kSplit) {
+    hipError_t e = c.kernel == 0 ? mla::launch_split_bf16(c.a, c.waves, c.groups, stream)
+                                 : mla::launch_split_fp8_topk(c.a, c.waves, c.groups, stream);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  if ((stages & kCombine) && c.a.nsplit > 1) {
+    if (mla::launch_combine(c.a, stream) != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_verify_attn(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table, const int32_t* seq_lens,
+                    const mla_mask_t* mask_desc, float* out, float* lse, int nsplit, hipStream_t stream) {
+  return run(q, kv_cache, slot_table, seq_lens, mask_desc, out, lse, nsplit, stream, kBoth);
+}
+
+int mla_verify_split(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table, const int32_t* seq_lens,
+                     const mla_mask_t* mask_desc, float* out, float* lse, int nsplit, hipStream_t stream) {
+  return run(q, kv_cache, slot_table, seq_lens, mask_desc, out, lse, nsplit, stream, kSplit);
+}
+
+int mla_verify_combine(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table,
+                       const int32_t* seq_lens, const mla_mask_t* mask_desc, float* out, float* lse, int nsplit,
+                       hipStream_t stream) {
+  return run(q, kv_cache, slot_table, seq_lens, mask_desc, out, lse, nsplit, stream, kCombine);
+}
+
+int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_desc, int nsplit, mla_plan_t* plan) {
+  if (!plan) return MLA_ERR_INVALID_ARG;
+  int st = validate(q, kv_cache, nullptr, nullptr, mask_desc, nullptr, nullptr, nsplit, false);
+  if (st != MLA_OK) return st;
+  int cus = 256;
+  int dev = 0;
+  if (nsplit <= 0 && current_device(&dev) == MLA_OK) cus = device_cus(dev);
+  Call c;
+  if ((st = make_plan(q, kv_cache, mask_desc, nsplit, cus, &c)) != MLA_OK) return st;
+  plan->nsplit = c.a.nsplit;
+  plan->waves_per_group = c.waves;
+  plan->row_groups = c.groups;
+  plan->grid = c.a.nsplit * c.groups * q->batch;
+  plan->workspace_bytes = c.ws_bytes;
+  plan->kernel = c.kernel;
+  return MLA_OK;
+}
+
+int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus) {
+  if (batch < 1 || q_len < 1 || heads < 1 || max_seq_len < 0 || num_cus < 1) return MLA_ERR_INVALID_ARG;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+  return choose_nsplit_impl(batch, q_len, heads, max_seq_len, kv_dtype, num_cus);
+}
+
+size_t mla_workspace_bytes(int batch, int q_len, int heads, int nsplit) {
+  if (batch < 1 || q_len < 1 || heads < 1 || nsplit <= 1) return 0;
+  return (size_t)batch * nsplit * q_len * heads * (kDv + 1) * sizeof(float);
+}
+
+int mla_reserve_workspace(size_t bytes, hipStream_t stream) {
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  unsigned* err = nullptr;
+  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  if (bytes == 0) return MLA_OK;
+  void* p = nullptr;
+  return workspace(dev, stream, bytes, &p);
+}
+
+int mla_build_tree_mask_host(const int32_t* parents, int batch, int q_len, uint64_t* anc_out) {
+  if (!parents || !anc_out || batch < 1 || q_len < 1) return MLA_ERR_INVALID_ARG;
+  if (q_len > MLA_MAX_Q_LEN) return MLA_ERR_UNSUPPORTED;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t* par = parents + (size_t)b * q_len;
+    for (int i = 0; i < q_len; ++i) {
+      if (par[i] < -1 || par[i] >= i) return MLA_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < q_len; ++i) {
+      uint64_t bits = 1ull << i;
+      for (int p = par[i]; p != -1; p = par[p]) bits |= 1ull << p;
+      anc_out[(size_t)b * q_len + i] = bits;
+    }
+  }
+  return MLA_OK;
+}
+
+int mla_build_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* anc_out, hipStream_t stream) {
+  if (!parents || !anc_out || batch < 1 || q_len < 1) return MLA_ERR_INVALID_ARG;
+  if (q_len > MLA_MAX_Q_LEN) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(parents, 4) || !aligned(anc_out, 8)) return MLA_ERR_ALIGN;
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  unsigned* err = nullptr;
+  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  return mla::launch_tree_mask(parents, batch, q_len, anc_out, err, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int mla_get_device_error(int clear) {
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  unsigned* err = nullptr;
+  if ((st = error_word(dev, nullptr, &err)) != MLA_OK) return st;
+  if (hipDeviceSynchronize() != hipSuccess) return MLA_ERR_LAUNCH;
+  unsigned v = 0;
+  if (hipMemcpy(&v, err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (clear && hipMemset(err, 0, sizeof(unsigned)) != hipSuccess) return MLA_ERR_LAUNCH;
+  return (int)(v & 0x7fffffffu);
+}
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_ALIGN: return "pointer misaligned";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or combination";
+    case MLA_ERR_WORKSPACE: return "workspace too small while the stream is capturing";
+    case MLA_ERR_LAUNCH: return "HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mla_abi_version(void) { return MLA_VERIFY_ABI_VERSION; }
+
+}  // extern "C"

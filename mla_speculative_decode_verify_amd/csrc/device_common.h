@@ -1,0 +1,51 @@
+// Device-side building blocks for gfx950 (CDNA4): MFMA wrappers, the LDS
+// transposing read, fast exp2/log2 and wave64 cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// D = A * B + C for A 16x32, B 32x16 (bf16), C/D 16x16 fp32.
+// Lane l holds A[l % 16][8*(l/16) .. +7], B[8*(l/16) .. +7][l % 16] and
+// C[4*(l/16) + r][l % 16] for r = 0..3 (checked on gfx950).
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read. Within each 16-lane group, lane 4*b + c supplies the
+// address of 4 consecutive 16-bit elements of "row" b (b, c in 0..3); lane i
+// of the group receives element i of the 16-element span, taken from rows
+// 0..3 in order. The address must be 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Max / sum across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ void flag_error(unsigned* err, unsigned bits) {
+  if (err) atomicOr(err, bits);
+}
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+}  // namespace mla

@@ -1,0 +1,50 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the kernel
+// translation units. Not installed; the public ABI is include/mla_verify.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDk = 576;    // absorbed query / key width (512 latent ++ 64 rope)
+constexpr int kDv = 512;    // value width: the latent part of the same row
+constexpr int kDrope = 64;
+
+// Everything a kernel needs, with pointers already validated by the host.
+struct Args {
+  const void* q;            // bf16 [batch, rows, 576]
+  const void* latent;       // bf16 [pool, 576] or e4m3 [pool, 512]
+  const void* rope;         // bf16 [pool, 64] (fp8 cache only)
+  const float* kscale;      // fp32 [pool] (fp8 cache only)
+  const int32_t* slots;     // [batch, slot_stride]
+  const int32_t* seq_lens;  // [batch]
+  const uint64_t* anc;      // [batch, q_len] (tree)
+  const int32_t* topk_idx;  // [batch, q_len, topk] (sparse)
+  float* out;               // [batch, rows, 512]
+  float* lse;               // [batch, rows] or nullptr
+  float* part_o;            // [batch, nsplit, rows, 512]
+  float* part_lse;          // [batch, nsplit, rows]
+  unsigned* err;            // device error flag word
+  const void* zero_row;     // >= 1152 zero bytes, read in place of masked / invalid cache rows
+  int64_t pool_rows;
+  int slot_stride;
+  int batch, q_len, heads, rows;  // rows = q_len * heads
+  int nsplit;
+  int mask_kind;
+  int topk;
+  float scale_log2;         // sm_scale * log2(e)
+};
+
+// Split kernels. `waves` = 16-row blocks per workgroup, `row_groups` = workgroups
+// along the row axis. Grid = nsplit * row_groups * batch.
+hipError_t launch_split_bf16(const Args& a, int waves, int row_groups, hipStream_t stream);
+hipError_t launch_split_fp8_topk(const Args& a, int waves, int row_groups, hipStream_t stream);
+// Log-sum-exp merge of the partials into out / lse.
+hipError_t launch_combine(const Args& a, hipStream_t stream);
+// Ancestor-or-self masks from parent arrays.
+hipError_t launch_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* anc, unsigned* err,
+                            hipStream_t stream);
+
+}  // namespace mla

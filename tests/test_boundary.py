@@ -1,0 +1,144 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+declared entry point, rejects bad arguments before any HIP call, and its
+host-side helpers (tree masks, split choice, workspace size) are exact."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mla_speculative_decode_verify_amd import binding as B
+from oracle import mla_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+pytestmark = pytest.mark.cpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmla_verify.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mla_verify.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/mla_verify.h but not exported"
+    assert B.abi_version() == 1
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert B.status_string(code) and B.status_string(code) != "unknown status"
+    assert B.status_string(-99) == "unknown status"
+
+
+# A fake but 16-byte aligned, non-null "device pointer": validation must fail
+# before the library ever dereferences or launches with it.
+FAKE = 0x10000
+
+
+def call(q_over=None, kv_over=None, mask_over=None, nsplit=0, out=FAKE, lse=None, slots=FAKE, seq=FAKE):
+    q = dict(data=FAKE, batch=1, q_len=9, heads=8, sm_scale=0.07)
+    kv = dict(dtype=B.MLA_KV_BF16, latent=FAKE, rope=None, scale=None, pool_rows=100, slot_stride=50, max_seq_len=0)
+    m = dict(kind=1, tree_anc=None, topk_idx=None, topk=0)
+    q.update(q_over or {})
+    kv.update(kv_over or {})
+    m.update(mask_over or {})
+    qd, kd, md = B.MlaQ(**q), B.MlaKV(**kv), B.MlaMask(**m)
+    return B.lib().mla_verify_attn(ctypes.byref(qd), ctypes.byref(kd), slots, seq, ctypes.byref(md), out, lse,
+                                   nsplit, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_over=dict(data=None)), B.MLA_ERR_INVALID_ARG),
+    (dict(out=None), B.MLA_ERR_INVALID_ARG),
+    (dict(slots=None), B.MLA_ERR_INVALID_ARG),
+    (dict(q_over=dict(batch=0)), B.MLA_ERR_INVALID_ARG),
+    (dict(q_over=dict(q_len=0)), B.MLA_ERR_INVALID_ARG),
+    (dict(q_over=dict(q_len=65)), B.MLA_ERR_UNSUPPORTED),
+    (dict(q_over=dict(heads=129)), B.MLA_ERR_UNSUPPORTED),
+    (dict(q_over=dict(sm_scale=0.0)), B.MLA_ERR_INVALID_ARG),
+    (dict(q_over=dict(sm_scale=float("inf"))), B.MLA_ERR_INVALID_ARG),
+    (dict(q_over=dict(data=FAKE + 8)), B.MLA_ERR_ALIGN),
+    (dict(out=FAKE + 4), B.MLA_ERR_ALIGN),
+    (dict(lse=FAKE + 2), B.MLA_ERR_ALIGN),
+    (dict(slots=FAKE + 2), B.MLA_ERR_ALIGN),
+    (dict(kv_over=dict(latent=FAKE + 8)), B.MLA_ERR_ALIGN),
+    (dict(kv_over=dict(pool_rows=0)), B.MLA_ERR_INVALID_ARG),
+    (dict(kv_over=dict(max_seq_len=51)), B.MLA_ERR_INVALID_ARG),
+    (dict(kv_over=dict(dtype=7)), B.MLA_ERR_INVALID_ARG),
+    (dict(mask_over=dict(kind=9)), B.MLA_ERR_INVALID_ARG),
+    (dict(mask_over=dict(kind=2)), B.MLA_ERR_INVALID_ARG),             # tree without masks
+    (dict(mask_over=dict(kind=2, tree_anc=FAKE + 4)), B.MLA_ERR_ALIGN),
+    (dict(mask_over=dict(kind=3)), B.MLA_ERR_UNSUPPORTED),             # top-k on a bf16 cache
+    (dict(nsplit=1025), B.MLA_ERR_INVALID_ARG),
+    (dict(kv_over=dict(dtype=1, rope=FAKE, scale=FAKE)), B.MLA_ERR_UNSUPPORTED),  # fp8 needs top-k
+    (dict(kv_over=dict(dtype=1, rope=FAKE, scale=FAKE), mask_over=dict(kind=3, topk_idx=FAKE, topk=0)),
+     B.MLA_ERR_INVALID_ARG),
+    (dict(kv_over=dict(dtype=1, rope=None, scale=FAKE), mask_over=dict(kind=3, topk_idx=FAKE, topk=8)),
+     B.MLA_ERR_INVALID_ARG),
+    (dict(kv_over=dict(dtype=1, rope=FAKE + 8, scale=FAKE), mask_over=dict(kind=3, topk_idx=FAKE, topk=8)),
+     B.MLA_ERR_ALIGN),
+])
+def test_bad_arguments_rejected_before_launch(L, kw, code):
+    assert call(**kw) == code
+
+
+def test_null_descriptors(L):
+    assert L.mla_verify_attn(None, None, None, None, None, None, None, 0, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_plan(None, None, None, 0, None) == B.MLA_ERR_INVALID_ARG
+
+
+def test_choose_nsplit_rules(L):
+    # one tensor-parallel rank's share: H=8, q_len 9 -> 72 rows, one row group
+    assert B.choose_nsplit(1, 9, 8, 65545, num_cus=256) == 256
+    assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 129      # capped: >= 128 keys per split
+    assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 29       # 9 row groups of 64 rows
+    assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 1
+    assert B.choose_nsplit(32, 1, 64, 2048, kv_dtype=B.MLA_KV_FP8_E4M3, num_cus=256) == 8
+    for args in [(0, 9, 8, 10, 0, 256), (1, 9, 8, -1, 0, 256), (1, 9, 8, 10, 5, 256), (1, 9, 8, 10, 0, 0)]:
+        assert L.mla_choose_nsplit(*args) == B.MLA_ERR_INVALID_ARG
+
+
+def test_plan_shapes(L):
+    p = B.plan(1, 9, 8, 16393, nsplit=64)
+    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"]) == (64, 5, 1, 64)
+    assert p["workspace_bytes"] == 64 * 72 * 513 * 4
+    p = B.plan(1, 9, 64, 4105, nsplit=16)
+    assert (p["waves_per_group"], p["row_groups"], p["grid"]) == (4, 9, 144)
+    p = B.plan(2, 1, 1, 10, nsplit=1)
+    assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 1
+
+
+def test_workspace_bytes(L):
+    assert B.workspace_bytes(1, 9, 8, 1) == 0
+    assert B.workspace_bytes(3, 9, 8, 16) == 3 * 16 * 72 * 513 * 4
+
+
+def test_host_tree_mask_bit_exact_vs_oracle(L):
+    rng = np.random.default_rng(0)
+    for q_len in (1, 2, 9, 31, 64):
+        par = np.array([[rng.integers(-1, i) if i else -1 for i in range(q_len)] for _ in range(7)], dtype=np.int32)
+        np.testing.assert_array_equal(B.build_tree_mask_host(par), O.ancestor_masks(par))
+    chain = np.array([[i - 1 for i in range(64)]], dtype=np.int32)
+    np.testing.assert_array_equal(B.build_tree_mask_host(chain), O.causal_masks(1, 64))
+
+
+def test_host_tree_mask_rejects_bad_parents(L):
+    for bad in ([[0]], [[-1, 1]], [[-1, -2]], [[-1, 0, 5]]):
+        with pytest.raises(B.MlaError) as e:
+            B.build_tree_mask_host(np.array(bad, dtype=np.int32))
+        assert e.value.status == B.MLA_ERR_INVALID_ARG
+    with pytest.raises(B.MlaError):
+        B.build_tree_mask_host(np.zeros((1, 65), dtype=np.int32) - 1)
