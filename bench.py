@@ -1,0 +1,230 @@
+"""Benchmark of MLA speculative-decoding verify attention on one MI355X.
+
+Prints ONE JSON line on stdout (everything else goes to stderr).
+
+Step = one verify call through the C ABI (plan + split kernel + combine
+kernel) over one batch of seeded synthetic inputs already resident in HBM.
+The headline workload is one tensor-parallel rank's share at long context:
+batch 1, q_len 9 draft queries, H=8 heads, prefix 65536, bf16 latent cache
+in a page_size=1 pool of 2x the tokens addressed through a random-permutation
+slot table, causal draft mask. Timing is cold-cache: consecutive calls rotate
+over disjoint copies of the cache (> 1 GiB in total) so neither the 4 MiB L2s
+nor the 256 MiB Infinity Cache hold the next call's rows.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_64k]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn µs/call + achieved TB/s & MFMA % (q_len 9, H=8/64, 16k-64k prefix)"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3_64k")
+    ap.add_argument("--nsplit", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough for > 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def describe(w):
+    if w.kind == "sparse":
+        return (f"{w.name}: batch {w.batch}, q_len {w.q_len}, H {w.heads}, prefix {w.meta['prefix']}, "
+                f"fp8 e4m3 latent + bf16 rope, top-k {w.meta['topk']}, page_size=1 random slots")
+    pre = w.meta["prefixes"]
+    pre_s = str(pre[0]) if len(set(pre)) == 1 else f"{min(pre)}..{max(pre)}"
+    return (f"{w.name}: batch {w.batch}, q_len {w.q_len}, H {w.heads}, prefix {pre_s}, bf16 latent, "
+            f"page_size=1 {'random' if w.meta['layout'] == 'random' else 'contiguous'} slots, {w.mask} mask")
+
+
+class Rotation:
+    """`copies` disjoint device copies of one verify workload's cache."""
+
+    def __init__(self, w, copies, nsplit, stage_list=("both", "split", "combine")):
+        import numpy as np
+        import torch
+
+        from mla_speculative_decode_verify_amd import binding as B
+
+        dev = "cuda"
+        self.w = w
+        rows = w.pool_rows
+        pool = torch.empty((copies * rows, 576), dtype=torch.bfloat16, device=dev)
+        base = torch.from_numpy(w.pool_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        for c in range(copies):
+            pool[c * rows:(c + 1) * rows].copy_(base)
+        del base
+        self.pool = pool
+        self.q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.seq = torch.from_numpy(w.seq_lens).to(dev)
+        self.anc = None
+        if w.mask == "tree":
+            self.anc = B.build_tree_mask(torch.from_numpy(w.parents).to(dev))
+        self.slots = [torch.from_numpy((w.slot_table.astype(np.int64) + c * rows).astype(np.int32)).to(dev)
+                      for c in range(copies)]
+        self.out = torch.empty((w.batch, w.q_len, w.heads, 512), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((w.batch, w.q_len, w.heads), dtype=torch.float32, device=dev)
+        self.calls = {}
+        for stage in stage_list:
+            self.calls[stage] = [B.PreparedCall(self.q, kv=pool, slot_table=s, seq_lens=self.seq,
+                                                sm_scale=w.sm_scale, mask=w.mask, tree_anc=self.anc, out=self.out,
+                                                lse=self.lse, nsplit=nsplit, stage=stage) for s in self.slots]
+        p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=nsplit, mask=w.mask)
+        self.plan = p
+        B.reserve_workspace(p["workspace_bytes"])
+
+
+def time_calls(calls, steps, warmup, rotate=True):
+    """Average µs per call over `steps` calls (events on torch's current stream)."""
+    import torch
+
+    n = len(calls)
+    for i in range(warmup):
+        calls[i % n if rotate else 0]()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        calls[i % n if rotate else 0]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def cpu_baseline(w, reps=3):
+    import numpy as np
+
+    from oracle import mla_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    anc = O.causal_masks(w.batch, w.q_len) if w.mask == "causal" else (
+        O.ancestor_masks(w.parents) if w.mask == "tree" else None)
+    ts = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        O.verify_attention(w.q_bits, w.pool_bits, w.slot_table, w.seq_lens, anc, w.sm_scale)
+        ts.append(time.perf_counter() - t)
+    return dict(value=statistics.median(ts) * 1e6, unit="us/call", cores=int(threads), kind="oracle",
+                sample=f"the full {w.name} call (all {w.batch * w.q_len * w.heads} query rows), median of {reps}")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mla_speculative_decode_verify_amd import binding as B
+    from mla_speculative_decode_verify_amd import inputs as I
+    from mla_speculative_decode_verify_amd import roofline as RL
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B.lib()
+    w = I.workload(args.workload)
+    if w.kind != "verify":
+        raise SystemExit("bench.py times bf16 verify workloads")
+    read_bytes = w.seq_lens.astype("int64").sum() * 1152
+    copies = args.copies or max(2, int(-(-(1 << 30) // int(read_bytes))) + 1)
+    log(f"[bench] {describe(w)}; copies {copies}")
+    rot = Rotation(w, copies, args.nsplit)
+    plan = rot.plan
+    log(f"[bench] plan {plan}")
+
+    cold = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=True)
+    warm = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=False)
+    split_us = time_calls(rot.calls["split"], args.steps, args.warmup, rotate=True)
+    comb_us = time_calls(rot.calls["combine"], args.steps, args.warmup, rotate=True) if plan["nsplit"] > 1 else 0.0
+    log(f"[bench] cold {cold:.2f} us/call, warm {warm:.2f}, split kernel {split_us:.2f}, combine {comb_us:.2f}")
+
+    cnt = RL.verify_counts(w.q_len, w.heads, w.seq_lens.tolist(), mask=w.mask,
+                           parents=None if w.parents is None else w.parents.tolist())
+    rf = RL.roofline_us(cnt["flops"], cnt["bytes"])
+    achieved_gbps = cnt["bytes"] / (split_us * 1e-6) / 1e9
+    peak = RL.PEAK_HBM_GBPS if rf["bound"] == "hbm" else RL.PEAK_BF16_TFLOPS
+    ach = achieved_gbps if rf["bound"] == "hbm" else cnt["flops"] / (split_us * 1e-6) / 1e12
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        try:
+            tr = json.load(open(PROFILE_TRAFFIC))
+            key = f"{w.name}/nsplit{plan['nsplit']}"
+            if key in tr and tr[key].get("kernel_source_hash") == kernel_hash():
+                traffic = tr[key]["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    roof = dict(bound=rf["bound"], achieved=round(ach, 2), peak=peak, unit="GB/s" if rf["bound"] == "hbm" else "TFLOP/s",
+                frac=round(ach / peak, 4), traffic=traffic)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(w)
+        log(f"[bench] oracle {cpu['value']:.0f} us/call on {cpu['cores']} threads")
+    line = {
+        "metric": METRIC,
+        "value": round(cold, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(cold / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 queries and latent rows, random page_size=1 slot permutation",
+        "config": {"workload": describe(w), "batch": w.batch, "q_len": w.q_len, "heads": w.heads,
+                   "prefix": w.meta["prefixes"][0] if len(set(w.meta["prefixes"])) == 1 else w.meta["prefixes"],
+                   "nsplit": plan["nsplit"], "waves_per_group": plan["waves_per_group"],
+                   "row_groups": plan["row_groups"], "grid": plan["grid"], "cold_copies": copies},
+        "warm_us": round(warm, 3),
+        "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3)},
+        "achieved_TBps": round(cnt["bytes"] / (cold * 1e-6) / 1e12, 4),
+        "achieved_TFLOPs": round(cnt["flops"] / (cold * 1e-6) / 1e12, 3),
+        "mfma_frac_of_peak": round(cnt["flops"] / (cold * 1e-6) / 1e12 / RL.PEAK_BF16_TFLOPS, 5),
+        "roofline_us": round(rf["us"], 3),
+        "algorithmic": {"bytes": cnt["bytes"], "flops": cnt["flops"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def kernel_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "mla_speculative_decode_verify_amd", "csrc"))):
+        h.update(open(os.path.join(ROOT, "mla_speculative_decode_verify_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

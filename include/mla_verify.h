@@ -127,11 +127,12 @@ typedef struct mla_mask_t {
 /* Plan of one call, as chosen by the library (for tests and measurement). */
 typedef struct mla_plan_t {
   int nsplit;            /* KV splits per sequence actually used */
-  int waves_per_group;   /* wavefronts (16 query rows each) per workgroup */
+  int waves_per_group;   /* wavefronts per workgroup (two per 16-row query block) */
   int row_groups;        /* workgroups along the query-row axis per split */
   int grid;              /* split-kernel workgroups */
   size_t workspace_bytes;/* partial storage needed (0 when nsplit == 1) */
   int kernel;            /* 0 = bf16 verify, 1 = fp8 top-k sparse */
+  int row_blocks;        /* 16-row query blocks per workgroup */
 } mla_plan_t;
 
 /*

@@ -61,7 +61,8 @@ class MlaMask(ctypes.Structure):
 
 class MlaPlan(ctypes.Structure):
     _fields_ = [("nsplit", ctypes.c_int), ("waves_per_group", ctypes.c_int), ("row_groups", ctypes.c_int),
-                ("grid", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int)]
+                ("grid", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int),
+                ("row_blocks", ctypes.c_int)]
 
 
 _lib = None
@@ -286,3 +287,37 @@ def device_error(clear: bool = True) -> int:
 
 def abi_version() -> int:
     return lib().mla_abi_version()
+
+
+class PreparedCall:
+    """A verify / sparse-decode call with its descriptors marshalled once.
+
+    ``__call__`` re-issues exactly the same C call (same tensors, same stream
+    handle unless one is given) with no per-call Python validation, for
+    tight timing loops and graph capture. The tensors must stay alive.
+    """
+
+    def __init__(self, q, *, kv=None, latent=None, rope=None, scale=None, slot_table, seq_lens, sm_scale,
+                 mask="causal", tree_anc=None, topk_idx=None, out=None, lse=None, nsplit=0, max_seq_len=0,
+                 stage="both"):
+        import torch
+
+        if kv is not None:
+            self.qd, self.kd, self.md, shape = _descs(q, MLA_KV_BF16, kv, None, None, slot_table, mask, tree_anc,
+                                                      None, sm_scale, max_seq_len)
+        else:
+            self.qd, self.kd, self.md, shape = _descs(q, MLA_KV_FP8_E4M3, latent, rope, scale, slot_table, "topk",
+                                                      None, topk_idx, sm_scale, max_seq_len)
+        _req(seq_lens, torch.int32, "seq_lens", (shape[0],))
+        self.out, self.lse = _outputs(shape, out, lse, True, q.device)
+        self._keep = (q, kv, latent, rope, scale, slot_table, seq_lens, tree_anc, topk_idx)
+        self.fn = getattr(lib(), _STAGES[stage])
+        self.args = (ctypes.byref(self.qd), ctypes.byref(self.kd), ctypes.c_void_p(slot_table.data_ptr()),
+                     ctypes.c_void_p(seq_lens.data_ptr()), ctypes.byref(self.md),
+                     ctypes.c_void_p(self.out.data_ptr()), ctypes.c_void_p(self.lse.data_ptr()), int(nsplit))
+        self.what = _STAGES[stage]
+
+    def __call__(self, stream_handle: Optional[int] = None):
+        st = self.fn(*self.args, _stream_handle(None) if stream_handle is None else stream_handle)
+        if st != MLA_OK:
+            raise MlaError(st, self.what)

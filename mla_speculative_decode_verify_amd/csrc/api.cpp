@@ -106,33 +106,31 @@ int workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
 }
 
 // ----------------------------------------------------------------- planning
-// Query rows are cut into 16-row blocks (one wavefront each); a workgroup
-// takes `waves` blocks. Prefer no padding; then 4 or 8 waves (even SIMD load).
-void choose_row_groups(int rows, int* waves, int* groups) {
+// Query rows are cut into 16-row blocks; a workgroup serves `nb` blocks with
+// two wavefronts each (split_bf16.hip), at most 5 blocks (10 wavefronts).
+// Pick the grouping with the least padded work, preferring 4 blocks (two
+// wavefronts per SIMD) on ties.
+void choose_row_groups(int rows, int* nb, int* groups) {
   const int blocks = (rows + 15) / 16;
-  if (blocks <= 8) {
-    *waves = blocks;
+  if (blocks <= 5) {
+    *nb = blocks;
     *groups = 1;
     return;
   }
-  int best_w = 8, best_pad = 1 << 30;
-  const int order[] = {4, 8, 6, 5, 7};
-  for (int w : order) {
-    const int g = (blocks + w - 1) / w;
-    const int pad = g * w - blocks;
-    if (pad < best_pad) {
-      best_pad = pad;
-      best_w = w;
-    }
+  const int g4 = (blocks + 3) / 4, g5 = (blocks + 4) / 5;
+  if (g5 * 5 < g4 * 4) {
+    *nb = 5;
+    *groups = g5;
+  } else {
+    *nb = 4;
+    *groups = g4;
   }
-  *waves = best_w;
-  *groups = (blocks + best_w - 1) / best_w;
 }
 
 int choose_nsplit_impl(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus) {
   if (batch < 1 || q_len < 1 || heads < 1 || num_cus < 1) return 1;
-  int waves, groups;
-  choose_row_groups(q_len * heads, &waves, &groups);
+  int nb, groups;
+  choose_row_groups(q_len * heads, &nb, &groups);
   const long wgs_per_split = (long)batch * groups;
   // Aim at one workgroup per CU; never fewer than 4 tiles (128 keys) per split.
   long s = (num_cus + wgs_per_split - 1) / wgs_per_split;
@@ -145,7 +143,7 @@ int choose_nsplit_impl(int batch, int q_len, int heads, int max_seq_len, int kv_
 
 struct Call {
   mla::Args a;
-  int waves = 1, groups = 1;
+  int nb = 1, groups = 1;
   int kernel = 0;
   size_t ws_bytes = 0;
 };
@@ -187,7 +185,7 @@ int validate(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, co
 
 int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsplit, int num_cus, Call* c) {
   const int rows = q->q_len * q->heads;
-  choose_row_groups(rows, &c->waves, &c->groups);
+  choose_row_groups(rows, &c->nb, &c->groups);
   c->kernel = kv->dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
   const int maxlen = kv->max_seq_len > 0 ? kv->max_seq_len : kv->slot_stride;
   const int seqlen_for_split = c->kernel == 1 ? std::min(maxlen, m->topk) : maxlen;
@@ -249,8 +247,8 @@ int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const i
     c.a.part_lse = static_cast<float*>(ws) + n_o;
   }
   if (stages & kSplit) {
-    hipError_t e = c.kernel == 0 ? mla::launch_split_bf16(c.a, c.waves, c.groups, stream)
-                                 : mla::launch_split_fp8_topk(c.a, c.waves, c.groups, stream);
+    hipError_t e = c.kernel == 0 ? mla::launch_split_bf16(c.a, c.nb, c.groups, stream)
+                                 : mla::launch_split_fp8_topk(c.a, c.nb, c.groups, stream);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   if ((stages & kCombine) && c.a.nsplit > 1) {
@@ -289,11 +287,12 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
   Call c;
   if ((st = make_plan(q, kv_cache, mask_desc, nsplit, cus, &c)) != MLA_OK) return st;
   plan->nsplit = c.a.nsplit;
-  plan->waves_per_group = c.waves;
+  plan->waves_per_group = 2 * c.nb;
   plan->row_groups = c.groups;
   plan->grid = c.a.nsplit * c.groups * q->batch;
   plan->workspace_bytes = c.ws_bytes;
   plan->kernel = c.kernel;
+  plan->row_blocks = c.nb;
   return MLA_OK;
 }
 

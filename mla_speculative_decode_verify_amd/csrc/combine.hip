@@ -17,50 +17,73 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// One wavefront per row; each lane owns 8 of the 512 output columns.
+// One workgroup per (sequence, query row, 128-column quarter). The four
+// wavefronts take every fourth split; each lane owns 2 of the 128 columns
+// (512 contiguous bytes per wavefront and split). Partial sums meet in LDS.
+constexpr int kCombCols = 128;
+constexpr int kCombWaves = 4;
+
 __global__ __launch_bounds__(256) void combine_kernel(Args a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
-  const int b = blockIdx.y;
+  __shared__ float red_max[kCombWaves];
+  __shared__ float red_sum[kCombWaves];
+  __shared__ float2 red_acc[kCombWaves - 1][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int quarter = blockIdx.x, row = blockIdx.y, b = blockIdx.z;
   const int S = a.nsplit, R = a.rows;
-  if (row >= R) return;
-  const float* pl = a.part_lse + (size_t)b * S * R + row;  // stride R between splits
+  const float* pl = a.part_lse + (size_t)b * S * R + row;  // split s at pl[s * R]
+
   float mx = -INFINITY;
-  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, pl[(size_t)s * R]);
+  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, pl[(size_t)s * R]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red_max[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  float2 acc = {0.f, 0.f};
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    const float* po = a.part_o + ((size_t)b * S * R + row) * kDv + lane * 8;
     const size_t sstride = (size_t)R * kDv;
-    int s = 0;
-    for (; s + 2 <= S; s += 2) {
-      const float l0 = pl[(size_t)s * R], l1 = pl[(size_t)(s + 1) * R];
-      const float w0 = fast_exp2((l0 - mx) * kLog2e);  // -inf -> 0
-      const float w1 = fast_exp2((l1 - mx) * kLog2e);
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(po + s * sstride);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(po + s * sstride + 4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(po + (s + 1) * sstride);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(po + (s + 1) * sstride + 4);
-      wsum += w0 + w1;
-      acc0 += w0 * a0 + w1 * b0;
-      acc1 += w0 * a1 + w1 * b1;
+    const float* po = a.part_o + ((size_t)b * S * R + row) * kDv + quarter * kCombCols + lane * 2;
+    int s = wave;
+    for (; s + 3 * kCombWaves < S; s += 4 * kCombWaves) {
+      float w[4];
+      float2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int su = s + u * kCombWaves;
+        w[u] = fast_exp2((pl[(size_t)su * R] - mx) * kLog2e);  // -inf -> 0
+        v[u] = *reinterpret_cast<const float2*>(po + su * sstride);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wsum += w[u];
+        acc.x += w[u] * v[u].x;
+        acc.y += w[u] * v[u].y;
+      }
     }
-    if (s < S) {
-      const float l0 = pl[(size_t)s * R];
-      const float w0 = fast_exp2((l0 - mx) * kLog2e);
-      wsum += w0;
-      acc0 += w0 * *reinterpret_cast<const f32x4*>(po + s * sstride);
-      acc1 += w0 * *reinterpret_cast<const f32x4*>(po + s * sstride + 4);
+    for (; s < S; s += kCombWaves) {
+      const float w = fast_exp2((pl[(size_t)s * R] - mx) * kLog2e);
+      const float2 v = *reinterpret_cast<const float2*>(po + s * sstride);
+      wsum += w;
+      acc.x += w * v.x;
+      acc.y += w * v.y;
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  float* dst = a.out + ((size_t)b * R + row) * kDv + lane * 8;
-  *reinterpret_cast<f32x4*>(dst) = acc0 * inv;
-  *reinterpret_cast<f32x4*>(dst + 4) = acc1 * inv;
-  if (lane == 0 && a.lse) a.lse[(size_t)b * R + row] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 : -INFINITY;
+  if (lane == 0) red_sum[wave] = wsum;
+  if (wave > 0) red_acc[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  const float tot = red_sum[0] + red_sum[1] + red_sum[2] + red_sum[3];
+#pragma unroll
+  for (int k = 0; k < kCombWaves - 1; ++k) {
+    acc.x += red_acc[k][lane].x;
+    acc.y += red_acc[k][lane].y;
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  float* dst = a.out + ((size_t)b * R + row) * kDv + quarter * kCombCols + lane * 2;
+  *reinterpret_cast<float2*>(dst) = float2{acc.x * inv, acc.y * inv};
+  if (quarter == 0 && lane == 0 && a.lse) a.lse[(size_t)b * R + row] = tot > 0.f ? mx + fast_log2(tot) * kLn2 : -INFINITY;
 }
 
 // One thread per (sequence, draft): walk the parent chain to the root.
@@ -93,7 +116,7 @@ __global__ void tree_mask_kernel(const int32_t* parents, int batch, int q_len, u
 }  // namespace
 
 hipError_t launch_combine(const Args& a, hipStream_t stream) {
-  dim3 grid((a.rows + 3) / 4, a.batch);
+  dim3 grid(kDv / kCombCols, a.rows, a.batch);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -42,6 +42,34 @@ __device__ __forceinline__ float group4_sum(float v) {
   return v;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations (lgkmcnt) and meets the other waves, but unlike __syncthreads()
+// does not drain the vector-memory queue, so global loads and global-to-LDS
+// gathers stay in flight across it. Callers wait for any global-to-LDS data
+// they need with an explicit vmcnt wait first. The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Global-to-LDS load of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane i's 16 bytes land at LDS byte address lds_addr + 16 i, where lds_addr
+// is wave-uniform (it goes through M0). Written as inline assembly so the
+// compiler neither tracks these loads nor inserts its own waits for them:
+// callers count them and wait with an explicit vmcnt before reading the data,
+// and must drain them (vmcnt(0)) before the workgroup ends.
+__device__ __forceinline__ void lds_dma_b128(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 __device__ __forceinline__ void flag_error(unsigned* err, unsigned bits) {
   if (err) atomicOr(err, bits);
 }

@@ -37,10 +37,11 @@ struct Args {
   float scale_log2;         // sm_scale * log2(e)
 };
 
-// Split kernels. `waves` = 16-row blocks per workgroup, `row_groups` = workgroups
-// along the row axis. Grid = nsplit * row_groups * batch.
-hipError_t launch_split_bf16(const Args& a, int waves, int row_groups, hipStream_t stream);
-hipError_t launch_split_fp8_topk(const Args& a, int waves, int row_groups, hipStream_t stream);
+// Split kernels. `blocks` = 16-row query blocks per workgroup (two wavefronts
+// each), `row_groups` = workgroups along the row axis. Grid = nsplit *
+// row_groups * batch.
+hipError_t launch_split_bf16(const Args& a, int blocks, int row_groups, hipStream_t stream);
+hipError_t launch_split_fp8_topk(const Args& a, int blocks, int row_groups, hipStream_t stream);
 // Log-sum-exp merge of the partials into out / lse.
 hipError_t launch_combine(const Args& a, hipStream_t stream);
 // Ancestor-or-self masks from parent arrays.

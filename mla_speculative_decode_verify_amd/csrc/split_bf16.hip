@@ -1,24 +1,41 @@
 // Split-KV verify attention over a bf16 latent cache (page_size = 1), gfx950.
 //
-// One workgroup handles one (sequence, KV split, row group). A row group is
-// NW blocks of 16 query rows (row = draft * heads + head); each wavefront owns
-// one block: its 16 absorbed query rows stay in VGPRs for the whole split and
-// its 16 x 512 fp32 output accumulator lives in registers.
+// One workgroup handles one (sequence, KV split, row group). Query rows are
+// row = draft * heads + head, cut into blocks of 16 (one MFMA tile); a row
+// group is NB blocks. Every block is served by a PAIR of wavefronts: half 0
+// owns k-steps 0..8 of the 576-wide score dot product and output columns
+// 0..255, half 1 owns k-steps 9..17 and columns 256..511. Each half computes
+// a partial S over its k-steps, the two partials meet in LDS (summed in a
+// fixed order so both halves hold bitwise the same scores), both run the
+// same online softmax, and each accumulates its own 256 output columns. A
+// wavefront therefore keeps only 36 query registers and a 16 x 256 fp32
+// accumulator, which leaves room for two or three wavefronts per SIMD: the
+// hardware hides LDS and MFMA latency by switching between them.
 //
 // Per tile of 32 cache positions:
-//   1. gather: every thread loads 16-byte pieces of the 32 latent rows through
-//      the slot table (coalesced 16 B loads; each 1152 B row is 72 pieces)
-//      into registers one tile ahead, then stores them to an LDS tile
-//      [32][576 + 8 pad] that all wavefronts share. The rows are read from
-//      HBM once per row group, not once per head ("The Occupancy Epiphany",
-//      section "The Per-Head Design": head-tile amortisation of the KV loads).
-//   2. S^T = K Q^T on MFMA 16x16x32 bf16: 2 key blocks x 18 k-steps.
-//   3. draft mask (only in tiles that reach the drafts or the split end),
-//      online softmax in the log2 domain, probabilities rounded to bf16.
+//   1. gather: 16-byte pieces of the 32 latent rows (each 1152 B row is 72
+//      pieces) are loaded through the slot table straight into an LDS tile
+//      [32][576 + 8 pad] shared by all wavefronts, two tiles ahead of the
+//      one being consumed. The rows are read from HBM once per row group,
+//      not once per head ("The Occupancy Epiphany", section "The Per-Head
+//      Design": head-tile amortisation of the KV loads).
+//   2. partial S^T = K Q^T on MFMA 16x16x32 bf16 (2 key blocks x 9 k-steps).
+//   3. exchange partials, draft mask (only in tiles that reach the drafts or
+//      the split end), online softmax in the log2 domain, bf16 weights.
 //   4. O^T += V^T P^T on MFMA: V is the first 512 columns of the same LDS tile,
 //      read with the gfx950 transposing LDS load, so no second copy exists.
 // The epilogue writes the normalised partial output and its natural-log LSE
 // (or the final output when the call has one split).
+//
+// The gathers are issued as inline assembly and counted by hand: the compiler
+// would otherwise drain the whole load queue before every LDS read of a tile
+// (it cannot tell which buffer an in-flight global-to-LDS load writes). The
+// slot table of each chunk of up to 4096 positions is staged in LDS first, so
+// the only vector-memory operations inside the tile loop are the gathers.
+//
+// The running max is updated lazily: the exponent base only moves (and the
+// accumulators are only rescaled) when some row's max grows by more than
+// kRescaleSlack in log2 units, so weights stay below 2^kRescaleSlack.
 #include "device_common.h"
 #include "mla_internal.h"
 #include "mla_verify.h"
@@ -33,36 +50,80 @@ constexpr int kLdsStride = kRowPieces * 8;         // bf16 elements per LDS row
 constexpr int kTilePieces = kTile * kRowPieces;    // 2336
 constexpr int kSegments = (kTilePieces + 63) / 64; // 64-piece wave loads per tile (37)
 constexpr int kBufElems = kSegments * 64 * 8;      // one tile buffer incl. the tail segment
+constexpr int kHalfSteps = kDk / 32 / 2;           // 9 MFMA k-steps per half
+constexpr int kHalfBlocks = kDv / 16 / 2;          // 16 output column blocks per half
+constexpr int kStages = 3;                         // LDS tile buffers (two tiles in flight)
+constexpr int kSlotChunk = 4096;                   // slot table entries staged in LDS at a time
+constexpr float kRescaleSlack = 8.f;
 
 // Issue this wave's share of one tile's gather straight into LDS. Piece p of
 // the padded tile is row p / 73, column piece p % 73; each wave instruction
 // moves 64 consecutive pieces (1 KiB) from 64 independent 16-byte addresses.
-// Rows outside [lo, hi) or with a bad slot read the zero row instead, so the
-// tile never holds stale or poisoned data.
-__device__ __forceinline__ void gather_tile(__bf16* buf, int wave, int nw, int lane, int slot_vec,
-                                            const __bf16* pool, const __bf16* zero_row) {
-  for (int sg = wave; sg < kSegments; sg += nw) {
+// Slots come from the LDS-staged chunk (`slots_lds[key - chunk_lo]`) and are
+// validated here: rows at or past `hi`, or whose slot is outside the pool,
+// read the zero row instead, so a tile never holds stale or poisoned data.
+// Returns true if this lane saw an out-of-range slot.
+template <int NW>
+__device__ __forceinline__ bool gather_tile(__bf16* buf, int wave, int lane, const int* slots_lds, int chunk_lo,
+                                            int t0, int hi, int64_t pool_rows, const __bf16* pool,
+                                            const __bf16* zero_row) {
+  constexpr int kPer = (kSegments + NW - 1) / NW;
+  const uint32_t base = lds_addr_of(buf);
+  int slot[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {  // all slot reads first, then all gathers
+    const int p = (wave + k * NW) * 64 + lane;
+    slot[k] = slots_lds[min(t0 + p / kRowPieces, hi - 1) - chunk_lo];
+  }
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int sg = wave + k * NW;
     const int p = sg * 64 + lane;
     const int row = p / kRowPieces;
     const int part = min(p - row * kRowPieces, kPieces - 1);
-    const int slot = __shfl(slot_vec, row & 31);
-    const __bf16* src = slot >= 0 ? pool + (size_t)slot * kDk + part * 8 : zero_row + part * 8;
-    if (p < kTilePieces) {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(buf + sg * 512), 16, 0, 0);
-    }
+    const bool in_range = t0 + row < hi;
+    const bool slot_ok = slot[k] >= 0 && (int64_t)slot[k] < pool_rows;
+    bad |= in_range && !slot_ok;
+    const __bf16* src = (in_range && slot_ok) ? pool + (size_t)slot[k] * kDk + part * 8 : zero_row + part * 8;
+    if (sg < kSegments && p < kTilePieces) lds_dma_b128(src, __builtin_amdgcn_readfirstlane(base + sg * 1024));
   }
+  return bad;
 }
 
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void split_bf16_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) __bf16 kv[2 * kBufElems];
+__device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// V operand of the 16x16x32 MFMA for output columns [16 d, 16 d + 16): keys
+// 4g..4g+3 and 16+4g..16+4g+3 in k-slots 0..7 (matching the P operand).
+__device__ __forceinline__ bf16x8 v_operand(const __bf16* vT0, int d) {
+  const bf16x4 lo4 = lds_read_tr16(vT0 + 16 * d);
+  const bf16x4 hi4 = lds_read_tr16(vT0 + 16 * d + 16 * kLdsStride);
+  return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int NB>
+__global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
+  constexpr int NW = 2 * NB;
+  // Fewest gather instructions any wave issues per tile: waiting until at
+  // most that many are outstanding proves tile t has landed whenever tile
+  // t+1 was issued after it (loads retire in order).
+  constexpr int kWaitAhead = (kSegments / NW) < 63 ? (kSegments / NW) : 63;
+  __shared__ __attribute__((aligned(16))) __bf16 kv[kStages * kBufElems];  // tile ring
+  __shared__ __attribute__((aligned(16))) f32x4 spart[NW][2][64];          // partial scores per wave
+  __shared__ int slots_lds[kSlotChunk];                                    // slot table chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
+  const int half = wave & 1, blk = wave >> 1;
   const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
   const int S = a.nsplit, R = a.rows;
   const bool leader = (tid == 0) && (split == 0) && (grp == 0);
@@ -88,85 +149,59 @@ __global__ __launch_bounds__(NW * 64, 1) void split_bf16_kernel(Args a) {
   const int32_t* slot_row = a.slots + (size_t)b * a.slot_stride;
   const __bf16* pool = static_cast<const __bf16*>(a.latent);
   const __bf16* zero_row = static_cast<const __bf16*>(a.zero_row);
-  // lane k < 32 of every wave holds the slot of key t0 + k (-1: read zeros)
-  auto load_slots = [&](int t0) {
-    const int j = t0 + (lane & 31);
-    int s = -1;
-    if (j < hi) {
-      s = slot_row[j];
-      if (s < 0 || (int64_t)s >= a.pool_rows) {
-        flag_error(a.err, MLA_DEVERR_SLOT_RANGE);
-        s = -1;
-      }
-    }
-    return s;
-  };
 
-  // ---- start the first tile's gather before anything else
-  int slots_next = -1;
-  if (lo < hi) {
-    const int s0 = load_slots(lo);
-    gather_tile(kv, wave, NW, lane, s0, pool, zero_row);
-    if (lo + kTile < hi) slots_next = load_slots(lo + kTile);
-  }
-
-  // ---- this wavefront's 16 query rows
-  const int row0 = (grp * NW + wave) * 16;
-  const bool wave_active = row0 < R;
+  // ---- this wavefront's rows, draft-mask words and query k-steps
+  const int row0 = (grp * NB + blk) * 16;
+  const bool active = row0 < R;  // uniform per wavefront pair
   const int row = row0 + li;
-  const int rowc = row < R ? row : R - 1;
-  const int qi = rowc / a.heads;
-  uint64_t anc_bits = ~0ull;
-  if (a.mask_kind == MLA_MASK_CAUSAL) anc_bits = (2ull << qi) - 1ull;  // drafts 0..qi
-  else if (a.mask_kind == MLA_MASK_TREE) anc_bits = a.anc[(size_t)b * a.q_len + qi];
-  const uint32_t anc_lo = (uint32_t)anc_bits, anc_hi = (uint32_t)(anc_bits >> 32);
+  const int qi = min(row, R - 1) / a.heads;
+  uint64_t bits = ~0ull;
+  if (a.mask_kind == MLA_MASK_CAUSAL) bits = (2ull << qi) - 1ull;  // drafts 0..qi
+  else if (a.mask_kind == MLA_MASK_TREE) bits = a.anc[(size_t)b * a.q_len + qi];
+  const uint32_t anc_lo = (uint32_t)bits, anc_hi = (uint32_t)(bits >> 32);
 
-  bf16x8 qr[18];
+  bf16x8 qr[kHalfSteps];
   {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) +
-                                                       ((size_t)b * R + rowc) * kDk) + g;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)b * R + min(row, R - 1)) * kDk +
+                       32 * kHalfSteps * half + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qr[ks] = qp[ks * 4];
+    for (int ks = 0; ks < kHalfSteps; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
   }
+  wait_vmcnt<0>();  // queries in registers before any gather is in flight
 
-  f32x4 o[32];
+  f32x4 o[kHalfBlocks];
 #pragma unroll
-  for (int d = 0; d < 32; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max, log2 domain
-  float l = 0.f;        // this lane's share of the running sum of exp (gives the LSE)
-  float lr = 0.f;       // same sum over the bf16-rounded weights fed to the MFMA (normalises O)
+  for (int d = 0; d < kHalfBlocks; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // exponent base, log2 domain (a lower bound of the running max)
+  float l = 0.f;        // lane share of the running sum of exp (gives the LSE)
+  float lr = 0.f;       // same over the bf16-rounded weights fed to the MFMA (normalises O)
+  bool bad_slot = false;
 
-  // lane coordinates for the transposing V reads: row 4g + tb, column 4tc
-  const int tb = li >> 2, tc = li & 3;
-  const int offA = li * kLdsStride + 8 * g;
-  const int offV = (4 * g + tb) * kLdsStride + 4 * tc;
+  // lane offsets: K operand row li, columns 8g of this half's k-range;
+  // V operand row 4g + li / 4, columns 4 (li % 4) of this half's columns
+  const int offA = li * kLdsStride + 32 * kHalfSteps * half + 8 * g;
+  const int offV = (4 * g + (li >> 2)) * kLdsStride + 256 * half + 4 * (li & 3);
 
-  int buf = 0;
-  for (int t0 = lo; t0 < hi; t0 += kTile, buf ^= 1) {
-    wait_vm_all();     // this wave's pieces of tile t0 have landed
-    __syncthreads();   // ... and every other wave's; the other buffer is free
-    if (t0 + kTile < hi) {
-      const int s_cur = slots_next;
-      if (t0 + 2 * kTile < hi) slots_next = load_slots(t0 + 2 * kTile);
-      gather_tile(kv + (buf ^ 1) * kBufElems, wave, NW, lane, s_cur, pool, zero_row);
-    }
-    if (!wave_active) continue;
-    const __bf16* tile = kv + buf * kBufElems;
-    const __bf16* kA0 = tile + offA;
-    const __bf16* kA1 = kA0 + 16 * kLdsStride;
-    const __bf16* vT0 = tile + offV;
-    const __bf16* vT1 = vT0 + 16 * kLdsStride;
-
-    // ---- S^T[key][row] = K Q^T
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  auto compute_tile = [&](const __bf16* cur, int t0) {
+    // ---- partial S^T[key][row] over this half's 9 k-steps
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    if (active) {
+      const __bf16* kA0 = cur + offA;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kA0 + 32 * ks);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kA1 + 32 * ks);
-      s0 = mfma_16x16x32(k0, qr[ks], s0);
-      s1 = mfma_16x16x32(k1, qr[ks], s1);
+      for (int ks = 0; ks < kHalfSteps; ++ks) {
+        s0 = mfma_16x16x32(lds_read_b128(kA0 + 32 * ks), qr[ks], s0);
+        s1 = mfma_16x16x32(lds_read_b128(kA0 + 16 * kLdsStride + 32 * ks), qr[ks], s1);
+      }
+      spart[wave][0][lane] = s0;
+      spart[wave][1][lane] = s1;
     }
-    // lane holds row li, keys t0 + 16*kb + 4g + r
+    lds_barrier();  // both halves' partials are in LDS
+    if (!active) return;
+    const int w0 = wave & ~1;  // fixed summation order: half 0 + half 1
+    s0 = spart[w0][0][lane] + spart[w0 + 1][0][lane];
+    s1 = spart[w0][1][lane] + spart[w0 + 1][1][lane];
+
+    // ---- mask + online softmax (lane holds row li, keys t0 + 16 kb + 4g + r)
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -190,39 +225,75 @@ __global__ __launch_bounds__(NW * 64, 1) void split_bf16_kernel(Args a) {
 #pragma unroll
     for (int r = 1; r < 8; ++r) mx = fmaxf(mx, x[r]);
     mx = group4_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float base = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - base);
+    // move the base only when some row's max outgrew it by more than the slack
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      // 0 when the old base was -inf; rows still without a visible key keep alpha = 1
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+      lr *= alpha;
+#pragma unroll
+      for (int d = 0; d < kHalfBlocks; ++d) o[d] *= alpha;
+    }
+    const float base = (m == -INFINITY) ? 0.f : m;
     bf16x8 pv;
-    float psum = 0.f, psum_r = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float pf = fast_exp2(x[r] - base);
       const __bf16 pb = static_cast<__bf16>(pf);
       pv[r] = pb;
-      psum += pf;
-      psum_r += static_cast<float>(pb);
-    }
-    l = l * alpha + psum;
-    lr = lr * alpha + psum_r;
-    m = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int d = 0; d < 32; ++d) o[d] *= alpha;
+      l += pf;
+      lr += static_cast<float>(pb);
     }
 
-    // ---- O^T[dim][row] += V^T P^T
+    // ---- O^T[dim][row] += V^T P^T over this half's 16 column blocks
+    const __bf16* vT0 = cur + offV;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const bf16x4 lo4 = lds_read_tr16(vT0 + 16 * d);
-      const bf16x4 hi4 = lds_read_tr16(vT1 + 16 * d);
-      const bf16x8 va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[d] = mfma_16x16x32(va, pv, o[d]);
+    for (int d = 0; d < kHalfBlocks; ++d) o[d] = mfma_16x16x32(v_operand(vT0, d), pv, o[d]);
+  };
+
+  // ---- main loop: chunks of up to kSlotChunk positions, tiles pipelined two ahead
+  for (int cb = lo; cb < hi; cb += kSlotChunk) {
+    const int ce = min(hi, cb + kSlotChunk);
+    // stage the chunk's slots: batches of 8 loads per thread in flight at once
+    for (int i0 = 0; i0 < ce - cb; i0 += 8 * NW * 64) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * NW * 64 + tid;
+        v[u] = i < ce - cb ? slot_row[cb + i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * NW * 64 + tid;
+        if (i < ce - cb) slots_lds[i] = v[u];
+      }
     }
+    lds_barrier();  // slots visible to every wave
+    bad_slot |= gather_tile<NW>(kv, wave, lane, slots_lds, cb, cb, ce, a.pool_rows, pool, zero_row);
+    if (cb + kTile < ce)
+      bad_slot |= gather_tile<NW>(kv + kBufElems, wave, lane, slots_lds, cb, cb + kTile, ce, a.pool_rows, pool,
+                                  zero_row);
+    int buf = 0;
+    for (int t0 = cb; t0 < ce; t0 += kTile) {
+      if (t0 + kTile < ce) wait_vmcnt<kWaitAhead>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // tile t0 is in LDS for every wave; the buffer of tile t0 - 32 is free
+      if (t0 + 2 * kTile < ce) {
+        const int nb = buf == 0 ? kStages - 1 : buf - 1;
+        bad_slot |= gather_tile<NW>(kv + nb * kBufElems, wave, lane, slots_lds, cb, t0 + 2 * kTile, ce,
+                                    a.pool_rows, pool, zero_row);
+      }
+      compute_tile(kv + buf * kBufElems, t0);
+      buf = buf + 1 == kStages ? 0 : buf + 1;
+    }
+    lds_barrier();  // every wave is done with the tiles and the slot chunk
   }
+  if (bad_slot) flag_error(a.err, MLA_DEVERR_SLOT_RANGE);
 
-  if (!wave_active) return;
   // ---- epilogue: normalise and store this split's result
+  if (!active) return;
   const float lt = group4_sum(l);
   const float ltr = group4_sum(lr);
   const float inv = ltr > 0.f ? 1.f / ltr : 0.f;
@@ -238,31 +309,29 @@ __global__ __launch_bounds__(NW * 64, 1) void split_bf16_kernel(Args a) {
       dst = a.part_o + pr * kDv;
       lse_dst = a.part_lse + pr;
     }
+    dst += 256 * half + 4 * g;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) *reinterpret_cast<f32x4*>(dst + 16 * d + 4 * g) = o[d] * inv;
-    if (g == 0 && lse_dst) *lse_dst = lse_v;
+    for (int d = 0; d < kHalfBlocks; ++d) *reinterpret_cast<f32x4*>(dst + 16 * d) = o[d] * inv;
+    if (half == 0 && g == 0 && lse_dst) *lse_dst = lse_v;
   }
 }
 
-template <int NW>
-hipError_t launch_nw(const Args& a, int row_groups, hipStream_t stream) {
+template <int NB>
+hipError_t launch_nb(const Args& a, int row_groups, hipStream_t stream) {
   dim3 grid(a.nsplit, row_groups, a.batch);
-  hipLaunchKernelGGL(split_bf16_kernel<NW>, grid, dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL(split_bf16_kernel<NB>, grid, dim3(NB * 128), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_split_bf16(const Args& a, int waves, int row_groups, hipStream_t stream) {
-  switch (waves) {
-    case 1: return launch_nw<1>(a, row_groups, stream);
-    case 2: return launch_nw<2>(a, row_groups, stream);
-    case 3: return launch_nw<3>(a, row_groups, stream);
-    case 4: return launch_nw<4>(a, row_groups, stream);
-    case 5: return launch_nw<5>(a, row_groups, stream);
-    case 6: return launch_nw<6>(a, row_groups, stream);
-    case 7: return launch_nw<7>(a, row_groups, stream);
-    case 8: return launch_nw<8>(a, row_groups, stream);
+hipError_t launch_split_bf16(const Args& a, int blocks, int row_groups, hipStream_t stream) {
+  switch (blocks) {
+    case 1: return launch_nb<1>(a, row_groups, stream);
+    case 2: return launch_nb<2>(a, row_groups, stream);
+    case 3: return launch_nb<3>(a, row_groups, stream);
+    case 4: return launch_nb<4>(a, row_groups, stream);
+    case 5: return launch_nb<5>(a, row_groups, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -112,13 +112,15 @@ def test_choose_nsplit_rules(L):
 
 
 def test_plan_shapes(L):
-    p = B.plan(1, 9, 8, 16393, nsplit=64)
-    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"]) == (64, 5, 1, 64)
+    p = B.plan(1, 9, 8, 16393, nsplit=64)      # 72 rows: 5 blocks of 16, two wavefronts each
+    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (64, 10, 1, 64, 5)
     assert p["workspace_bytes"] == 64 * 72 * 513 * 4
     p = B.plan(1, 9, 64, 4105, nsplit=16)
-    assert (p["waves_per_group"], p["row_groups"], p["grid"]) == (4, 9, 144)
+    assert (p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (8, 9, 144, 4)
+    p = B.plan(1, 9, 16, 4105, nsplit=16)      # 144 rows = 9 blocks: groups of 5 + 4
+    assert (p["waves_per_group"], p["row_groups"], p["row_blocks"]) == (10, 2, 5)
     p = B.plan(2, 1, 1, 10, nsplit=1)
-    assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 1
+    assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 2
 
 
 def test_workspace_bytes(L):
