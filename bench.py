@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--nsplit", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough for > 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -182,6 +185,14 @@ def main():
             traffic = None
     roof = dict(bound=rf["bound"], achieved=round(ach, 2), peak=peak, unit="GB/s" if rf["bound"] == "hbm" else "TFLOP/s",
                 frac=round(ach / peak, 4), traffic=traffic)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

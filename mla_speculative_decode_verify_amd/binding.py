@@ -14,7 +14,9 @@ from typing import Optional
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_verify.so")
+# The in-tree build; MLA_VERIFY_LIB may name another build of the same library.
+LIB_PATH = os.environ.get("MLA_VERIFY_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "libmla_verify.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = -1

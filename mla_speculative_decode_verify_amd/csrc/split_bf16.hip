@@ -6,7 +6,8 @@
 // owns k-steps 0..8 of the 576-wide score dot product and output columns
 // 0..255, half 1 owns k-steps 9..17 and columns 256..511. Each half computes
 // a partial S over its k-steps, the two partials meet in LDS (summed in a
-// fixed order so both halves hold bitwise the same scores), both run the
+// fixed order so both halves hold bitwise the same scores; the two waves
+// synchronise through a per-wave sequence flag, not a workgroup barrier), both run the
 // same online softmax, and each accumulates its own 256 output columns. A
 // wavefront therefore keeps only 36 query registers and a 16 x 256 fp32
 // accumulator, which leaves room for two or three wavefronts per SIMD: the
@@ -15,7 +16,7 @@
 // Per tile of 32 cache positions:
 //   1. gather: 16-byte pieces of the 32 latent rows (each 1152 B row is 72
 //      pieces) are loaded through the slot table straight into an LDS tile
-//      [32][576 + 8 pad] shared by all wavefronts, two tiles ahead of the
+//      [32][576 + 16 pad] shared by all wavefronts, two tiles ahead of the
 //      one being consumed. The rows are read from HBM once per row group,
 //      not once per head ("The Occupancy Epiphany", section "The Per-Head
 //      Design": head-tile amortisation of the KV loads).
@@ -45,7 +46,10 @@ namespace {
 
 constexpr int kTile = 32;                          // cache positions per tile (2 MFMA key blocks)
 constexpr int kPieces = kDk / 8;                   // 16-byte pieces per latent row (72)
-constexpr int kRowPieces = kPieces + 1;            // + one pad piece: LDS row = 1168 B (spreads banks)
+#ifndef MLA_ROW_PAD_PIECES
+#define MLA_ROW_PAD_PIECES 2
+#endif
+constexpr int kRowPieces = kPieces + MLA_ROW_PAD_PIECES;  // 16-byte pad pieces per LDS row spread the banks
 constexpr int kLdsStride = kRowPieces * 8;         // bf16 elements per LDS row
 constexpr int kTilePieces = kTile * kRowPieces;    // 2336
 constexpr int kSegments = (kTilePieces + 63) / 64; // 64-piece wave loads per tile (37)
@@ -56,37 +60,51 @@ constexpr int kStages = 3;                         // LDS tile buffers (two tile
 constexpr int kSlotChunk = 4096;                   // slot table entries staged in LDS at a time
 constexpr float kRescaleSlack = 8.f;
 
-// Issue this wave's share of one tile's gather straight into LDS. Piece p of
-// the padded tile is row p / 73, column piece p % 73; each wave instruction
-// moves 64 consecutive pieces (1 KiB) from 64 independent 16-byte addresses.
-// Slots come from the LDS-staged chunk (`slots_lds[key - chunk_lo]`) and are
-// validated here: rows at or past `hi`, or whose slot is outside the pool,
-// read the zero row instead, so a tile never holds stale or poisoned data.
-// Returns true if this lane saw an out-of-range slot.
+// Per-lane geometry of one wave's share of a tile gather. Piece p of the
+// padded tile is row p / kRowPieces, column piece p % kRowPieces; each wave
+// instruction moves 64 consecutive pieces (1 KiB) from 64 independent 16-byte
+// addresses. Computed once per kernel; only the slot lookup changes per tile.
 template <int NW>
-__device__ __forceinline__ bool gather_tile(__bf16* buf, int wave, int lane, const int* slots_lds, int chunk_lo,
-                                            int t0, int hi, int64_t pool_rows, const __bf16* pool,
+struct GatherPlan {
+  static constexpr int kPer = (kSegments + NW - 1) / NW;
+  int row[kPer];       // tile row of this lane's piece (>= kTile: past the tile)
+  int part_off[kPer];  // element offset of the piece inside the latent row
+  __device__ __forceinline__ GatherPlan(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int sg = wave + k * NW;
+      const int p = sg * 64 + lane;
+      const bool live = sg < kSegments && p < kTilePieces;
+      row[k] = live ? p / kRowPieces : kTile;
+      part_off[k] = min(p - (p / kRowPieces) * kRowPieces, kPieces - 1) * 8;
+    }
+  }
+};
+
+// Issue this wave's share of one tile's gather straight into LDS. Slots come
+// from the LDS-staged chunk (`slots_lds[key - chunk_lo]`) and are validated
+// here: rows at or past `hi`, or whose slot is outside the pool
+// (`pool_lim` = min(pool_rows, 2^31)), read the zero row instead, so a tile
+// never holds stale or poisoned data. Returns true if this lane saw an
+// out-of-range slot.
+template <int NW>
+__device__ __forceinline__ bool gather_tile(__bf16* buf, int wave, const GatherPlan<NW>& gp, const int* slots_lds,
+                                            int chunk_lo, int t0, int hi, uint32_t pool_lim, const __bf16* pool,
                                             const __bf16* zero_row) {
-  constexpr int kPer = (kSegments + NW - 1) / NW;
+  constexpr int kPer = GatherPlan<NW>::kPer;
   const uint32_t base = lds_addr_of(buf);
   int slot[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {  // all slot reads first, then all gathers
-    const int p = (wave + k * NW) * 64 + lane;
-    slot[k] = slots_lds[min(t0 + p / kRowPieces, hi - 1) - chunk_lo];
-  }
+  for (int k = 0; k < kPer; ++k) slot[k] = slots_lds[min(t0 + gp.row[k], hi - 1) - chunk_lo];
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int sg = wave + k * NW;
-    const int p = sg * 64 + lane;
-    const int row = p / kRowPieces;
-    const int part = min(p - row * kRowPieces, kPieces - 1);
-    const bool in_range = t0 + row < hi;
-    const bool slot_ok = slot[k] >= 0 && (int64_t)slot[k] < pool_rows;
+    const bool in_range = t0 + gp.row[k] < hi;
+    const bool slot_ok = (uint32_t)slot[k] < pool_lim;
     bad |= in_range && !slot_ok;
-    const __bf16* src = (in_range && slot_ok) ? pool + (size_t)slot[k] * kDk + part * 8 : zero_row + part * 8;
-    if (sg < kSegments && p < kTilePieces) lds_dma_b128(src, __builtin_amdgcn_readfirstlane(base + sg * 1024));
+    const __bf16* src = (in_range && slot_ok) ? pool + (size_t)(uint32_t)slot[k] * kDk : zero_row;
+    if (gp.row[k] < kTile && wave + k * NW < kSegments)
+      lds_dma_b128(src + gp.part_off[k], __builtin_amdgcn_readfirstlane(base + (wave + k * NW) * 1024));
   }
   return bad;
 }
@@ -119,6 +137,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) __bf16 kv[kStages * kBufElems];  // tile ring
   __shared__ __attribute__((aligned(16))) f32x4 spart[NW][2][64];          // partial scores per wave
   __shared__ int slots_lds[kSlotChunk];                                    // slot table chunk
+  __shared__ int pair_seq[NW];  // last tile whose partial scores each wave has published
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -149,6 +168,8 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int32_t* slot_row = a.slots + (size_t)b * a.slot_stride;
   const __bf16* pool = static_cast<const __bf16*>(a.latent);
   const __bf16* zero_row = static_cast<const __bf16*>(a.zero_row);
+  const uint32_t pool_lim = (uint32_t)min<int64_t>(a.pool_rows, (int64_t)1 << 31);
+  const GatherPlan<NW> gp(wave, lane);
 
   // ---- this wavefront's rows, draft-mask words and query k-steps
   const int row0 = (grp * NB + blk) * 16;
@@ -182,6 +203,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int offA = li * kLdsStride + 32 * kHalfSteps * half + 8 * g;
   const int offV = (4 * g + (li >> 2)) * kLdsStride + 256 * half + 4 * (li & 3);
 
+  if (lane == 0) __hip_atomic_store(&pair_seq[wave], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  int seq = 0;                         // tiles processed by this workgroup
+
   auto compute_tile = [&](const __bf16* cur, int t0) {
     // ---- partial S^T[key][row] over this half's 9 k-steps
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -195,18 +219,26 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       spart[wave][0][lane] = s0;
       spart[wave][1][lane] = s1;
     }
-    lds_barrier();  // both halves' partials are in LDS
     if (!active) return;
+    // Publish this wave's partial, then wait for the partner wave's: only the
+    // pair synchronises here, not the workgroup. The partner publishes every
+    // tile too, so the wait ends; it cannot run a tile ahead because both
+    // must pass the next tile barrier first.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial stored before the flag
+    if (lane == 0) __hip_atomic_store(&pair_seq[wave], seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(&pair_seq[wave ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != seq)
+      __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
     const int w0 = wave & ~1;  // fixed summation order: half 0 + half 1
     s0 = spart[w0][0][lane] + spart[w0 + 1][0][lane];
     s1 = spart[w0][1][lane] + spart[w0 + 1][1][lane];
 
     // ---- mask + online softmax (lane holds row li, keys t0 + 16 kb + 4g + r)
-    float x[8];
+    float x[8];  // raw scores; the softmax scale (> 0) is applied inside the exponent
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r] = s0[r] * a.scale_log2;
-      x[4 + r] = s1[r] * a.scale_log2;
+      x[r] = s0[r];
+      x[4 + r] = s1[r];
     }
     if (t0 + kTile > hi || t0 + kTile > prefix) {
       // branch-free: key j is visible iff j < hi and (j is in the prefix or
@@ -224,7 +256,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     float mx = x[0];
 #pragma unroll
     for (int r = 1; r < 8; ++r) mx = fmaxf(mx, x[r]);
-    mx = group4_max(mx);
+    mx = group4_max(mx) * a.scale_log2;
     // move the base only when some row's max outgrew it by more than the slack
     if (__any(mx > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mx);
@@ -240,7 +272,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     bf16x8 pv;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const float pf = fast_exp2(x[r] - base);
+      const float pf = fast_exp2(fmaf(x[r], a.scale_log2, -base));
       const __bf16 pb = static_cast<__bf16>(pf);
       pv[r] = pb;
       l += pf;
@@ -271,10 +303,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       }
     }
     lds_barrier();  // slots visible to every wave
-    bad_slot |= gather_tile<NW>(kv, wave, lane, slots_lds, cb, cb, ce, a.pool_rows, pool, zero_row);
+    bad_slot |= gather_tile<NW>(kv, wave, gp, slots_lds, cb, cb, ce, pool_lim, pool, zero_row);
     if (cb + kTile < ce)
-      bad_slot |= gather_tile<NW>(kv + kBufElems, wave, lane, slots_lds, cb, cb + kTile, ce, a.pool_rows, pool,
-                                  zero_row);
+      bad_slot |= gather_tile<NW>(kv + kBufElems, wave, gp, slots_lds, cb, cb + kTile, ce, pool_lim, pool, zero_row);
     int buf = 0;
     for (int t0 = cb; t0 < ce; t0 += kTile) {
       if (t0 + kTile < ce) wait_vmcnt<kWaitAhead>();
@@ -282,10 +313,11 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       lds_barrier();  // tile t0 is in LDS for every wave; the buffer of tile t0 - 32 is free
       if (t0 + 2 * kTile < ce) {
         const int nb = buf == 0 ? kStages - 1 : buf - 1;
-        bad_slot |= gather_tile<NW>(kv + nb * kBufElems, wave, lane, slots_lds, cb, t0 + 2 * kTile, ce,
-                                    a.pool_rows, pool, zero_row);
+        bad_slot |= gather_tile<NW>(kv + nb * kBufElems, wave, gp, slots_lds, cb, t0 + 2 * kTile, ce, pool_lim,
+                                    pool, zero_row);
       }
       compute_tile(kv + buf * kBufElems, t0);
+      ++seq;
       buf = buf + 1 == kStages ? 0 : buf + 1;
     }
     lds_barrier();  // every wave is done with the tiles and the slot chunk
