@@ -60,8 +60,23 @@ def describe(w):
             f"page_size=1 {'random' if w.meta['layout'] == 'random' else 'contiguous'} slots, {w.mask} mask")
 
 
+def _replicate(host, copies, dtype=None):
+    """One device tensor holding `copies` back-to-back copies of a host array."""
+    import numpy as np
+    import torch
+
+    base = torch.from_numpy(np.ascontiguousarray(host))
+    if dtype is not None:
+        base = base.view(dtype)
+    base = base.to("cuda")
+    out = torch.empty((copies * base.shape[0],) + tuple(base.shape[1:]), dtype=base.dtype, device="cuda")
+    for c in range(copies):
+        out[c * base.shape[0]:(c + 1) * base.shape[0]].copy_(base)
+    return out
+
+
 class Rotation:
-    """`copies` disjoint device copies of one verify workload's cache."""
+    """`copies` disjoint device copies of one workload's cache, each addressed by its own slot table."""
 
     def __init__(self, w, copies, nsplit, stage_list=("both", "split", "combine")):
         import numpy as np
@@ -72,27 +87,37 @@ class Rotation:
         dev = "cuda"
         self.w = w
         rows = w.pool_rows
-        pool = torch.empty((copies * rows, 576), dtype=torch.bfloat16, device=dev)
-        base = torch.from_numpy(w.pool_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-        for c in range(copies):
-            pool[c * rows:(c + 1) * rows].copy_(base)
-        del base
-        self.pool = pool
         self.q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
         self.seq = torch.from_numpy(w.seq_lens).to(dev)
-        self.anc = None
-        if w.mask == "tree":
-            self.anc = B.build_tree_mask(torch.from_numpy(w.parents).to(dev))
         self.slots = [torch.from_numpy((w.slot_table.astype(np.int64) + c * rows).astype(np.int32)).to(dev)
                       for c in range(copies)]
         self.out = torch.empty((w.batch, w.q_len, w.heads, 512), dtype=torch.float32, device=dev)
         self.lse = torch.empty((w.batch, w.q_len, w.heads), dtype=torch.float32, device=dev)
         self.calls = {}
-        for stage in stage_list:
-            self.calls[stage] = [B.PreparedCall(self.q, kv=pool, slot_table=s, seq_lens=self.seq,
-                                                sm_scale=w.sm_scale, mask=w.mask, tree_anc=self.anc, out=self.out,
-                                                lse=self.lse, nsplit=nsplit, stage=stage) for s in self.slots]
-        p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=nsplit, mask=w.mask)
+        if w.kind == "verify":
+            self.pool = _replicate(w.pool_bits.view(np.int16), copies, torch.bfloat16)
+            self.anc = None
+            if w.mask == "tree":
+                self.anc = B.build_tree_mask(torch.from_numpy(w.parents).to(dev))
+            for stage in stage_list:
+                self.calls[stage] = [B.PreparedCall(self.q, kv=self.pool, slot_table=s, seq_lens=self.seq,
+                                                    sm_scale=w.sm_scale, mask=w.mask, tree_anc=self.anc,
+                                                    out=self.out, lse=self.lse, nsplit=nsplit, stage=stage)
+                                     for s in self.slots]
+            p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=nsplit, mask=w.mask)
+        else:
+            self.lat = _replicate(w.lat_bits, copies)
+            self.rope = _replicate(w.rope_bits.view(np.int16), copies, torch.bfloat16)
+            self.scale = _replicate(w.scale, copies)
+            self.topk = torch.from_numpy(w.topk_idx).to(dev)
+            for stage in stage_list:
+                self.calls[stage] = [B.PreparedCall(self.q, latent=self.lat, rope=self.rope, scale=self.scale,
+                                                    slot_table=s, seq_lens=self.seq, sm_scale=w.sm_scale,
+                                                    topk_idx=self.topk, out=self.out, lse=self.lse,
+                                                    nsplit=nsplit, stage=stage)
+                                     for s in self.slots]
+            p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, kv_dtype=B.MLA_KV_FP8_E4M3, mask="topk",
+                       topk=w.meta["topk"], nsplit=nsplit)
         self.plan = p
         B.reserve_workspace(p["workspace_bytes"])
 
@@ -126,12 +151,20 @@ def cpu_baseline(w, reps=3):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    anc = O.causal_masks(w.batch, w.q_len) if w.mask == "causal" else (
-        O.ancestor_masks(w.parents) if w.mask == "tree" else None)
+    if w.kind == "sparse":
+        def run():
+            O.sparse_decode_attention(w.q_bits, w.lat_bits, w.rope_bits, w.scale, w.slot_table, w.topk_idx,
+                                      w.sm_scale)
+    else:
+        anc = O.causal_masks(w.batch, w.q_len) if w.mask == "causal" else (
+            O.ancestor_masks(w.parents) if w.mask == "tree" else None)
+
+        def run():
+            O.verify_attention(w.q_bits, w.pool_bits, w.slot_table, w.seq_lens, anc, w.sm_scale)
     ts = []
     for _ in range(reps):
         t = time.perf_counter()
-        O.verify_attention(w.q_bits, w.pool_bits, w.slot_table, w.seq_lens, anc, w.sm_scale)
+        run()
         ts.append(time.perf_counter() - t)
     return dict(value=statistics.median(ts) * 1e6, unit="us/call", cores=int(threads), kind="oracle",
                 sample=f"the full {w.name} call (all {w.batch * w.q_len * w.heads} query rows), median of {reps}")
@@ -153,9 +186,13 @@ def main():
     torch.cuda.set_device(0)
     B.lib()
     w = I.workload(args.workload)
-    if w.kind != "verify":
-        raise SystemExit("bench.py times bf16 verify workloads")
-    read_bytes = w.seq_lens.astype("int64").sum() * 1152
+    if w.kind == "sparse":
+        cnt = RL.sparse_counts(w.batch, w.q_len, w.heads, w.meta["topk"])
+        read_bytes = w.batch * w.q_len * w.meta["topk"] * 652
+    else:
+        cnt = RL.verify_counts(w.q_len, w.heads, w.seq_lens.tolist(), mask=w.mask,
+                               parents=None if w.parents is None else w.parents.tolist())
+        read_bytes = w.seq_lens.astype("int64").sum() * 1152
     copies = args.copies or max(2, int(-(-(1 << 30) // int(read_bytes))) + 1)
     log(f"[bench] {describe(w)}; copies {copies}")
     rot = Rotation(w, copies, args.nsplit)
@@ -168,8 +205,6 @@ def main():
     comb_us = time_calls(rot.calls["combine"], args.steps, args.warmup, rotate=True) if plan["nsplit"] > 1 else 0.0
     log(f"[bench] cold {cold:.2f} us/call, warm {warm:.2f}, split kernel {split_us:.2f}, combine {comb_us:.2f}")
 
-    cnt = RL.verify_counts(w.q_len, w.heads, w.seq_lens.tolist(), mask=w.mask,
-                           parents=None if w.parents is None else w.parents.tolist())
     rf = RL.roofline_us(cnt["flops"], cnt["bytes"])
     achieved_gbps = cnt["bytes"] / (split_us * 1e-6) / 1e9
     peak = RL.PEAK_HBM_GBPS if rf["bound"] == "hbm" else RL.PEAK_BF16_TFLOPS
@@ -179,7 +214,7 @@ def main():
         try:
             tr = json.load(open(PROFILE_TRAFFIC))
             key = f"{w.name}/nsplit{plan['nsplit']}"
-            if key in tr and tr[key].get("kernel_source_hash") == kernel_hash():
+            if key in tr and tr[key].get("kernel_source_hash") == kernel_hash(w.kind):
                 traffic = tr[key]["bytes_per_launch"]
         except Exception:
             traffic = None
@@ -209,10 +244,14 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) bf16 queries and latent rows, random page_size=1 slot permutation",
+        "dtype": "bf16" if w.kind == "verify" else "fp8-e4m3 cache, bf16 MFMA",
+        "data": ("synthetic: seeded N(0,1) bf16 queries and latent rows, random page_size=1 slot permutation"
+                 if w.kind == "verify" else
+                 "synthetic: seeded N(0,1) bf16 queries, N(0,1) latent rounded to fp8 e4m3, bf16 rope, "
+                 "scales U[0.5,2], top-k positions drawn without replacement, random page_size=1 slots"),
         "config": {"workload": describe(w), "batch": w.batch, "q_len": w.q_len, "heads": w.heads,
-                   "prefix": w.meta["prefixes"][0] if len(set(w.meta["prefixes"])) == 1 else w.meta["prefixes"],
+                   "prefix": (w.meta["prefix"] if w.kind == "sparse" else
+                              w.meta["prefixes"][0] if len(set(w.meta["prefixes"])) == 1 else w.meta["prefixes"]),
                    "nsplit": plan["nsplit"], "waves_per_group": plan["waves_per_group"],
                    "row_groups": plan["row_groups"], "grid": plan["grid"], "cold_copies": copies},
         "warm_us": round(warm, 3),
@@ -228,11 +267,18 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def kernel_hash():
+KERNEL_SOURCES = {
+    "verify": ("split_bf16.hip", "device_common.h", "mla_internal.h"),
+    "sparse": ("split_fp8.hip", "device_common.h", "mla_internal.h"),
+}
+
+
+def kernel_hash(kind="verify"):
+    """Hash of the sources the split kernel of this workload kind is built from."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "mla_speculative_decode_verify_amd", "csrc"))):
+    for f in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, "mla_speculative_decode_verify_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

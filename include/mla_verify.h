@@ -177,7 +177,8 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
 
 /* Split count the library picks when nsplit <= 0: a pure function of the
  * shape and the CU count, so it is deterministic and safe under graph
- * capture. ("How One Environment Variable Unlocked 3x Throughput", section
+ * capture. max_seq_len is the longest sequence for a bf16 cache and the
+ * top-k list length for an fp8 cache (each query's list is split). ("How One Environment Variable Unlocked 3x Throughput", section
  * "The Occupancy Revelation": a small per-rank head count shrinks the grid
  * until the machine starves, and more splits refill it.) */
 int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus);

@@ -127,15 +127,35 @@ void choose_row_groups(int rows, int* nb, int* groups) {
   }
 }
 
-int choose_nsplit_impl(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus) {
+// Workgroups along the row axis and independent key sets per split: the
+// bf16 verify path groups all q_len * heads rows of a sequence (they share
+// its keys); the fp8 top-k path groups the heads of one query (each query
+// has its own key list), so its key sets are batch * q_len.
+// The fp8 kernel converts tiles in registers and spills with 5 blocks, so
+// its groups hold at most 4 blocks.
+void row_layout(int batch, int q_len, int heads, int kv_dtype, int* nb, int* groups, long* key_sets) {
+  if (kv_dtype == MLA_KV_FP8_E4M3) {
+    const int blocks = (heads + 15) / 16;
+    *nb = std::min(blocks, 4);
+    *groups = (blocks + *nb - 1) / *nb;
+    *key_sets = (long)batch * q_len;
+  } else {
+    choose_row_groups(q_len * heads, nb, groups);
+    *key_sets = batch;
+  }
+}
+
+// `keys` = positions per key set: the longest sequence (bf16 verify) or the
+// top-k list length (fp8 sparse).
+int choose_nsplit_impl(int batch, int q_len, int heads, int keys, int kv_dtype, int num_cus) {
   if (batch < 1 || q_len < 1 || heads < 1 || num_cus < 1) return 1;
   int nb, groups;
-  choose_row_groups(q_len * heads, &nb, &groups);
-  const long wgs_per_split = (long)batch * groups;
+  long key_sets;
+  row_layout(batch, q_len, heads, kv_dtype, &nb, &groups, &key_sets);
+  const long wgs_per_split = key_sets * groups;
   // Aim at one workgroup per CU; never fewer than 4 tiles (128 keys) per split.
   long s = (num_cus + wgs_per_split - 1) / wgs_per_split;
-  const long keys = kv_dtype == MLA_KV_FP8_E4M3 ? max_seq_len : max_seq_len;
-  const long cap = std::max<long>(1, (keys + 127) / 128);
+  const long cap = std::max<long>(1, ((long)keys + 127) / 128);
   s = std::min(s, cap);
   s = std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
   return (int)s;
@@ -184,8 +204,9 @@ int validate(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, co
 }
 
 int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsplit, int num_cus, Call* c) {
-  const int rows = q->q_len * q->heads;
-  choose_row_groups(rows, &c->nb, &c->groups);
+  long key_sets = 0;
+  row_layout(q->batch, q->q_len, q->heads, kv->dtype, &c->nb, &c->groups, &key_sets);
+  if (key_sets > 65535) return MLA_ERR_UNSUPPORTED;
   c->kernel = kv->dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
   const int maxlen = kv->max_seq_len > 0 ? kv->max_seq_len : kv->slot_stride;
   const int seqlen_for_split = c->kernel == 1 ? std::min(maxlen, m->topk) : maxlen;
@@ -289,7 +310,7 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
   plan->nsplit = c.a.nsplit;
   plan->waves_per_group = 2 * c.nb;
   plan->row_groups = c.groups;
-  plan->grid = c.a.nsplit * c.groups * q->batch;
+  plan->grid = c.a.nsplit * c.groups * q->batch * (c.kernel == 1 ? q->q_len : 1);
   plan->workspace_bytes = c.ws_bytes;
   plan->kernel = c.kernel;
   plan->row_blocks = c.nb;

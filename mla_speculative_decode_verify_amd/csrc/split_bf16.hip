@@ -82,13 +82,12 @@ struct GatherPlan {
 };
 
 // Issue this wave's share of one tile's gather straight into LDS. Slots come
-// from the LDS-staged chunk (`slots_lds[key - chunk_lo]`) and are validated
-// here: rows at or past `hi`, or whose slot is outside the pool
+// from the LDS-staged chunk (`slots_lds[key - chunk_lo]`, -1 where the slot
+// was outside the pool): rows at or past `hi`, or without a valid slot
 // (`pool_lim` = min(pool_rows, 2^31)), read the zero row instead, so a tile
-// never holds stale or poisoned data. Returns true if this lane saw an
-// out-of-range slot.
+// never holds stale or poisoned data.
 template <int NW>
-__device__ __forceinline__ bool gather_tile(__bf16* buf, int wave, const GatherPlan<NW>& gp, const int* slots_lds,
+__device__ __forceinline__ void gather_tile(__bf16* buf, int wave, const GatherPlan<NW>& gp, const int* slots_lds,
                                             int chunk_lo, int t0, int hi, uint32_t pool_lim, const __bf16* pool,
                                             const __bf16* zero_row) {
   constexpr int kPer = GatherPlan<NW>::kPer;
@@ -96,17 +95,14 @@ __device__ __forceinline__ bool gather_tile(__bf16* buf, int wave, const GatherP
   int slot[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) slot[k] = slots_lds[min(t0 + gp.row[k], hi - 1) - chunk_lo];
-  bool bad = false;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const bool in_range = t0 + gp.row[k] < hi;
     const bool slot_ok = (uint32_t)slot[k] < pool_lim;
-    bad |= in_range && !slot_ok;
     const __bf16* src = (in_range && slot_ok) ? pool + (size_t)(uint32_t)slot[k] * kDk : zero_row;
     if (gp.row[k] < kTile && wave + k * NW < kSegments)
       lds_dma_b128(src + gp.part_off[k], __builtin_amdgcn_readfirstlane(base + (wave + k * NW) * 1024));
   }
-  return bad;
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -206,7 +202,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   if (lane == 0) __hip_atomic_store(&pair_seq[wave], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   int seq = 0;                         // tiles processed by this workgroup
 
-  auto compute_tile = [&](const __bf16* cur, int t0) {
+  // chunk_bad: the staged chunk holds an invalid slot, so every tile of it
+  // takes the masked path, which also drops keys whose staged slot is -1.
+  auto compute_tile = [&](const __bf16* cur, int t0, int cb, int ce, bool chunk_bad) {
     // ---- partial S^T[key][row] over this half's 9 k-steps
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
     if (active) {
@@ -240,16 +238,17 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       x[r] = s0[r];
       x[4 + r] = s1[r];
     }
-    if (t0 + kTile > hi || t0 + kTile > prefix) {
-      // branch-free: key j is visible iff j < hi and (j is in the prefix or
-      // its draft bit is set for this row's query)
+    if (chunk_bad || t0 + kTile > hi || t0 + kTile > prefix) {
+      // branch-free: key j is visible iff j < hi, its slot is valid and (j is
+      // in the prefix or its draft bit is set for this row's query)
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int j = t0 + (r >> 2) * 16 + 4 * g + (r & 3);
         const int d = j - prefix;
         const uint32_t word = d < 32 ? anc_lo : anc_hi;
         const uint32_t bit = (word >> (d & 31)) & 1u;
-        const bool vis = (j < hi) & ((d < 0) | (bit != 0u));
+        const bool slot_ok = slots_lds[min(j, ce - 1) - cb] >= 0;
+        const bool vis = (j < hi) & slot_ok & ((d < 0) | (bit != 0u));
         x[r] = vis ? x[r] : -INFINITY;
       }
     }
@@ -289,6 +288,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   for (int cb = lo; cb < hi; cb += kSlotChunk) {
     const int ce = min(hi, cb + kSlotChunk);
     // stage the chunk's slots: batches of 8 loads per thread in flight at once
+    bool lane_bad = false;
     for (int i0 = 0; i0 < ce - cb; i0 += 8 * NW * 64) {
       int v[8];
 #pragma unroll
@@ -296,16 +296,24 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
         const int i = i0 + u * NW * 64 + tid;
         v[u] = i < ce - cb ? slot_row[cb + i] : 0;
       }
+      bool bad = false;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * NW * 64 + tid;
-        if (i < ce - cb) slots_lds[i] = v[u];
+        const bool ok = (uint32_t)v[u] < pool_lim;
+        bad |= (i < ce - cb) && !ok;
+        if (i < ce - cb) slots_lds[i] = ok ? v[u] : -1;
       }
+      lane_bad |= bad;
     }
-    lds_barrier();  // slots visible to every wave
-    bad_slot |= gather_tile<NW>(kv, wave, gp, slots_lds, cb, cb, ce, pool_lim, pool, zero_row);
+    bad_slot |= lane_bad;
+    // Slots visible to every wave, and whether any was invalid. No gather is
+    // in flight here (the previous chunk ended with a full drain), so the
+    // full barrier costs nothing.
+    const bool chunk_bad = __syncthreads_or(lane_bad) != 0;
+    gather_tile<NW>(kv, wave, gp, slots_lds, cb, cb, ce, pool_lim, pool, zero_row);
     if (cb + kTile < ce)
-      bad_slot |= gather_tile<NW>(kv + kBufElems, wave, gp, slots_lds, cb, cb + kTile, ce, pool_lim, pool, zero_row);
+      gather_tile<NW>(kv + kBufElems, wave, gp, slots_lds, cb, cb + kTile, ce, pool_lim, pool, zero_row);
     int buf = 0;
     for (int t0 = cb; t0 < ce; t0 += kTile) {
       if (t0 + kTile < ce) wait_vmcnt<kWaitAhead>();
@@ -313,10 +321,10 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       lds_barrier();  // tile t0 is in LDS for every wave; the buffer of tile t0 - 32 is free
       if (t0 + 2 * kTile < ce) {
         const int nb = buf == 0 ? kStages - 1 : buf - 1;
-        bad_slot |= gather_tile<NW>(kv + nb * kBufElems, wave, gp, slots_lds, cb, t0 + 2 * kTile, ce, pool_lim,
-                                    pool, zero_row);
+        gather_tile<NW>(kv + nb * kBufElems, wave, gp, slots_lds, cb, t0 + 2 * kTile, ce, pool_lim, pool,
+                        zero_row);
       }
-      compute_tile(kv + buf * kBufElems, t0);
+      compute_tile(kv + buf * kBufElems, t0, cb, ce, chunk_bad);
       ++seq;
       buf = buf + 1 == kStages ? 0 : buf + 1;
     }

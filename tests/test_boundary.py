@@ -123,6 +123,21 @@ def test_plan_shapes(L):
     assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 2
 
 
+def test_plan_shapes_fp8_topk(L):
+    fp8 = dict(kv_dtype=B.MLA_KV_FP8_E4M3, mask="topk", topk=2048)
+    p = B.plan(32, 1, 64, 65536, nsplit=8, **fp8)     # one query per sequence, 64 heads = 4 blocks
+    assert (p["kernel"], p["row_blocks"], p["row_groups"], p["grid"]) == (1, 4, 1, 8 * 32)
+    assert p["workspace_bytes"] == 32 * 8 * 64 * 513 * 4
+    p = B.plan(2, 3, 80, 5000, nsplit=2, **fp8)       # 5 blocks -> groups of at most 4; grid over (seq, query)
+    assert (p["row_blocks"], p["row_groups"], p["grid"]) == (4, 2, 2 * 2 * 2 * 3)
+    p = B.plan(1, 1, 8, 100, nsplit=1, **fp8)
+    assert (p["row_blocks"], p["waves_per_group"], p["workspace_bytes"]) == (1, 2, 0)
+    # auto split count: key sets are (sequence, query) pairs; >= 128 list entries per split
+    assert B.choose_nsplit(4, 3, 16, 512, kv_dtype=B.MLA_KV_FP8_E4M3) == 4
+    assert B.choose_nsplit(1, 1, 64, 65536, kv_dtype=B.MLA_KV_FP8_E4M3) == 256
+    assert B.plan(32, 1, 64, 65536, **fp8)["nsplit"] == 8
+
+
 def test_workspace_bytes(L):
     assert B.workspace_bytes(1, 9, 8, 1) == 0
     assert B.workspace_bytes(3, 9, 8, 16) == 3 * 16 * 72 * 513 * 4
