@@ -184,7 +184,8 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
 int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus);
 
 /* Bytes of split partials one call needs: batch * nsplit * q_len * heads *
- * (512 + 1) * 4, or 0 for nsplit <= 1. */
+ * (512 * 2 + 12) (fp16 partial output, its two power-of-two scales and the
+ * fp32 LSE per split and row), or 0 for nsplit <= 1. */
 size_t mla_workspace_bytes(int batch, int q_len, int heads, int nsplit);
 
 /* Make the workspace of (current device, stream) at least `bytes` long and

@@ -23,6 +23,8 @@ LIB = os.path.join(PKG, "libmla_verify.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "split_bf16.hip", "split_fp8.hip", "combine.hip"]
+# Per-source extra compiler flags.
+EXTRA_FLAGS = {}
 
 
 def hipcc() -> str:
@@ -40,7 +42,8 @@ def common_flags():
 
 def compile_one(src: str, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + [f"-D{d}" for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + [f"-D{d}" for d in defines] +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -234,6 +234,7 @@ void fill_args(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, 
   a.lse = lse;
   a.part_o = nullptr;
   a.part_lse = nullptr;
+  a.part_scale = nullptr;
   a.err = nullptr;
   a.zero_row = nullptr;
   a.pool_rows = kv->pool_rows;
@@ -263,9 +264,12 @@ int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const i
   if (c.a.nsplit > 1) {
     void* ws = nullptr;
     if ((st = workspace(dev, stream, c.ws_bytes, &ws)) != MLA_OK) return st;
-    const size_t n_o = (size_t)q->batch * c.a.nsplit * c.a.rows * kDv;
-    c.a.part_o = static_cast<float*>(ws);
-    c.a.part_lse = static_cast<float*>(ws) + n_o;
+    // [fp16 O: P x 512][fp32 LSE: P][fp32 scale: P x 2], P = batch * nsplit * rows
+    const size_t P = (size_t)q->batch * c.a.nsplit * c.a.rows;
+    char* base = static_cast<char*>(ws);
+    c.a.part_o = reinterpret_cast<_Float16*>(base);
+    c.a.part_lse = reinterpret_cast<float*>(base + P * kDv * sizeof(_Float16));
+    c.a.part_scale = c.a.part_lse + P;
   }
   if (stages & kSplit) {
     hipError_t e = c.kernel == 0 ? mla::launch_split_bf16(c.a, c.nb, c.groups, stream)
@@ -325,7 +329,7 @@ int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_d
 
 size_t mla_workspace_bytes(int batch, int q_len, int heads, int nsplit) {
   if (batch < 1 || q_len < 1 || heads < 1 || nsplit <= 1) return 0;
-  return (size_t)batch * nsplit * q_len * heads * (kDv + 1) * sizeof(float);
+  return (size_t)batch * nsplit * q_len * heads * (kDv * sizeof(_Float16) + 3 * sizeof(float));
 }
 
 int mla_reserve_workspace(size_t bytes, hipStream_t stream) {

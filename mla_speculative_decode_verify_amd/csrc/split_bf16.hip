@@ -40,6 +40,7 @@
 #include "device_common.h"
 #include "mla_internal.h"
 #include "mla_verify.h"
+#include "split_epilogue.h"
 
 namespace mla {
 namespace {
@@ -338,22 +339,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const float ltr = group4_sum(lr);
   const float inv = ltr > 0.f ? 1.f / ltr : 0.f;
   const float lse_v = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
-  if (row < R) {
-    float* dst;
-    float* lse_dst;
-    if (S == 1) {
-      dst = a.out + ((size_t)b * R + row) * kDv;
-      lse_dst = a.lse ? a.lse + (size_t)b * R + row : nullptr;
-    } else {
-      const size_t pr = ((size_t)b * S + split) * R + row;
-      dst = a.part_o + pr * kDv;
-      lse_dst = a.part_lse + pr;
-    }
-    dst += 256 * half + 4 * g;
-#pragma unroll
-    for (int d = 0; d < kHalfBlocks; ++d) *reinterpret_cast<f32x4*>(dst + 16 * d) = o[d] * inv;
-    if (half == 0 && g == 0 && lse_dst) *lse_dst = lse_v;
-  }
+  store_block_half(a, o, inv, lse_v, b, split, min(row, R - 1), half, g, row < R, half == 0 && g == 0);
 }
 
 template <int NB>

@@ -1,0 +1,60 @@
+// Epilogue shared by the split kernels: one wavefront's half of a finished
+// 16-row block goes either to the final output (single split) or to the
+// split-partial workspace.
+//
+// Partials are stored compactly: the normalised output O_s of each (split,
+// row) as fp16, with one power-of-two multiplier per 256-column half chosen
+// so the half's largest magnitude lands in [2^14, 2^15). The stored values
+// therefore never overflow fp16 and keep its full 11-bit precision whatever
+// the cache's value range (a relative error of at most 2^-12 per element,
+// well below the bf16 rounding of the weights), at half the bytes of fp32.
+// The LSE stays fp32.
+#pragma once
+
+#include "device_common.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Lane (g, li) holds o[d][r] (d < 16) = unnormalised output column
+// 256 half + 16 d + 4 g + r of block row li; `inv` normalises it.
+// All 64 lanes must call this (it reduces across lanes); `row_ok` says
+// whether row li exists. `r_out` is the row index within the sequence.
+__device__ __forceinline__ void store_block_half(const Args& a, const f32x4* o, float inv, float lse_v,
+                                                 int b, int split, int r_out, int half, int g, bool row_ok,
+                                                 bool write_lse) {
+  constexpr int kBlocks = kDv / 32;  // 16 column blocks of 16 per half
+  const int S = a.nsplit, R = a.rows;
+  if (S == 1) {
+    if (!row_ok) return;
+    float* dst = a.out + ((size_t)b * R + r_out) * kDv + 256 * half + 4 * g;
+#pragma unroll
+    for (int d = 0; d < kBlocks; ++d) *reinterpret_cast<f32x4*>(dst + 16 * d) = o[d] * inv;
+    if (write_lse && a.lse) a.lse[(size_t)b * R + r_out] = lse_v;
+    return;
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int d = 0; d < kBlocks; ++d)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(o[d][r] * inv));
+  mx = group4_max(mx);
+  // exponent of the half's largest magnitude (NaN / inf propagate unchanged)
+  const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127;
+  const int e = min(max(ex - 14, -126), 113);
+  const float down = __builtin_amdgcn_ldexpf(inv, -e);
+  if (!row_ok) return;
+  const size_t pr = ((size_t)b * S + split) * R + r_out;
+  _Float16* dst = a.part_o + pr * kDv + 256 * half + 4 * g;
+#pragma unroll
+  for (int d = 0; d < kBlocks; ++d) {
+    const f32x4 v = o[d] * down;
+    *reinterpret_cast<f16x4*>(dst + 16 * d) = __builtin_convertvector(v, f16x4);
+  }
+  if (g == 0) a.part_scale[pr * 2 + half] = __builtin_amdgcn_ldexpf(1.f, e);
+  if (write_lse) a.part_lse[pr] = lse_v;
+}
+
+}  // namespace mla

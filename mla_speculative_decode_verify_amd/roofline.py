@@ -87,10 +87,11 @@ def sparse_counts(batch: int, q_len: int, heads: int, topk: int) -> dict:
 
 
 def split_partial_bytes(batch: int, rows_per_seq: int, nsplit: int) -> float:
-    """Overhead traffic of the split partials: written once and read once (fp32 O and LSE)."""
+    """Overhead traffic of the split partials: written once and read once (fp16 O,
+    two fp32 power-of-two scales and the fp32 LSE per split and row)."""
     if nsplit <= 1:
         return 0.0
-    return 2.0 * batch * nsplit * rows_per_seq * (DV + 1) * 4
+    return 2.0 * batch * nsplit * rows_per_seq * (DV * 2 + 12)
 
 
 def roofline_us(flops: float, bytes_: float, peak_tflops: float = PEAK_BF16_TFLOPS,

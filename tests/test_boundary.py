@@ -114,7 +114,7 @@ def test_choose_nsplit_rules(L):
 def test_plan_shapes(L):
     p = B.plan(1, 9, 8, 16393, nsplit=64)      # 72 rows: 5 blocks of 16, two wavefronts each
     assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (64, 10, 1, 64, 5)
-    assert p["workspace_bytes"] == 64 * 72 * 513 * 4
+    assert p["workspace_bytes"] == 64 * 72 * 1036
     p = B.plan(1, 9, 64, 4105, nsplit=16)
     assert (p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (8, 9, 144, 4)
     p = B.plan(1, 9, 16, 4105, nsplit=16)      # 144 rows = 9 blocks: groups of 5 + 4
@@ -127,7 +127,7 @@ def test_plan_shapes_fp8_topk(L):
     fp8 = dict(kv_dtype=B.MLA_KV_FP8_E4M3, mask="topk", topk=2048)
     p = B.plan(32, 1, 64, 65536, nsplit=8, **fp8)     # one query per sequence, 64 heads = 4 blocks
     assert (p["kernel"], p["row_blocks"], p["row_groups"], p["grid"]) == (1, 4, 1, 8 * 32)
-    assert p["workspace_bytes"] == 32 * 8 * 64 * 513 * 4
+    assert p["workspace_bytes"] == 32 * 8 * 64 * 1036
     p = B.plan(2, 3, 80, 5000, nsplit=2, **fp8)       # 5 blocks -> groups of at most 4; grid over (seq, query)
     assert (p["row_blocks"], p["row_groups"], p["grid"]) == (4, 2, 2 * 2 * 2 * 3)
     p = B.plan(1, 1, 8, 100, nsplit=1, **fp8)
@@ -140,7 +140,7 @@ def test_plan_shapes_fp8_topk(L):
 
 def test_workspace_bytes(L):
     assert B.workspace_bytes(1, 9, 8, 1) == 0
-    assert B.workspace_bytes(3, 9, 8, 16) == 3 * 16 * 72 * 513 * 4
+    assert B.workspace_bytes(3, 9, 8, 16) == 3 * 16 * 72 * 1036
 
 
 def test_host_tree_mask_bit_exact_vs_oracle(L):

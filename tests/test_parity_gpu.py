@@ -124,3 +124,23 @@ def test_split_and_combine_stages_equal_full_call():
     d.run(nsplit=4, stage="combine", out=o2, lse=l2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("factor", [1.0e5, 1.0e-4])
+def test_partials_keep_value_range(factor):
+    # Cache values far above the fp16 range (or far below 1): the split
+    # partials carry a per-half power-of-two scale, so the merged result
+    # matches the oracle to the usual tolerances once rescaled. The softmax
+    # scale is divided by the same factor so the scores keep their spread.
+    w = I.make_verify("range", batch=2, q_len=9, heads=8, prefixes=[900, 2000], seed=33, layout="random")
+    vals = O.bf16_bits_to_f64(w.pool_bits) * factor
+    pool = I.f32_to_bf16_bits(vals.astype(np.float32))
+    w2 = I.VerifyInputs(**{**w.__dict__, "pool_bits": pool, "sm_scale": w.sm_scale / factor})
+    ref_out, ref_lse = oracle(w2)
+    d = DeviceInputs(w2)
+    for ns in (1, 7, 64):
+        _log(f"[parity] range factor={factor} nsplit={ns}")
+        out, lse = d.run(nsplit=ns)
+        torch.cuda.synchronize()
+        compare(out / factor, lse, ref_out / factor, ref_lse, f"range {factor} nsplit={ns}")
+    assert B.device_error() == 0
