@@ -60,26 +60,35 @@ constexpr int kHalfBlocks = kDv / 16 / 2;          // 16 output column blocks pe
 constexpr int kStages = 3;                         // LDS tile buffers (two tiles in flight)
 constexpr int kSlotChunk = 4096;                   // slot table entries staged in LDS at a time
 constexpr float kRescaleSlack = 8.f;
+#ifndef MLA_KAHEAD
+#define MLA_KAHEAD 2
+#endif
+constexpr int kAhead = MLA_KAHEAD;                 // LDS fragments read ahead of their MFMAs
 
 // Per-lane geometry of one wave's share of a tile gather. Piece p of the
 // padded tile is row p / kRowPieces, column piece p % kRowPieces; each wave
 // instruction moves 64 consecutive pieces (1 KiB) from 64 independent 16-byte
-// addresses. Computed once per kernel; only the slot lookup changes per tile.
+// addresses. Computed once per kernel and packed as 16 bits per piece,
+// (row << 10) | piece column, two pieces per register; only the slot lookup
+// changes per tile.
 template <int NW>
 struct GatherPlan {
   static constexpr int kPer = (kSegments + NW - 1) / NW;
-  int row[kPer];       // tile row of this lane's piece (>= kTile: past the tile)
-  int part_off[kPer];  // element offset of the piece inside the latent row
+  uint32_t packed[(kPer + 1) / 2];  // row >= kTile: past the tile
   __device__ __forceinline__ GatherPlan(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < (kPer + 1) / 2; ++k) packed[k] = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int sg = wave + k * NW;
       const int p = sg * 64 + lane;
       const bool live = sg < kSegments && p < kTilePieces;
-      row[k] = live ? p / kRowPieces : kTile;
-      part_off[k] = min(p - (p / kRowPieces) * kRowPieces, kPieces - 1) * 8;
+      const int row = live ? p / kRowPieces : kTile;
+      const uint32_t v = (uint32_t)(row << 10) | (uint32_t)min(p - (p / kRowPieces) * kRowPieces, kPieces - 1);
+      packed[k / 2] |= v << (16 * (k & 1));
     }
   }
+  __device__ __forceinline__ uint32_t get(int k) const { return (packed[k / 2] >> (16 * (k & 1))) & 0xFFFFu; }
 };
 
 // Issue this wave's share of one tile's gather straight into LDS. Slots come
@@ -93,16 +102,19 @@ __device__ __forceinline__ void gather_tile(__bf16* buf, int wave, const GatherP
                                             const __bf16* zero_row) {
   constexpr int kPer = GatherPlan<NW>::kPer;
   const uint32_t base = lds_addr_of(buf);
-  int slot[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) slot[k] = slots_lds[min(t0 + gp.row[k], hi - 1) - chunk_lo];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const bool in_range = t0 + gp.row[k] < hi;
-    const bool slot_ok = (uint32_t)slot[k] < pool_lim;
-    const __bf16* src = (in_range && slot_ok) ? pool + (size_t)(uint32_t)slot[k] * kDk : zero_row;
-    if (gp.row[k] < kTile && wave + k * NW < kSegments)
-      lds_dma_b128(src + gp.part_off[k], __builtin_amdgcn_readfirstlane(base + (wave + k * NW) * 1024));
+    if (!(wave + k * NW < kSegments)) continue;  // wave-uniform
+    uint32_t v = gp.get(k);
+    // Opaque per tile, so the compiler recomputes the 64-bit source address
+    // instead of holding one per piece across the tile loop.
+    asm volatile("" : "+v"(v));
+    const int row = (int)(v >> 10);
+    const int slot = slots_lds[min(t0 + row, hi - 1) - chunk_lo];
+    const bool ok = (t0 + row < hi) && ((uint32_t)slot < pool_lim);
+    const __bf16* rowp = ok ? pool + (size_t)(uint32_t)slot * kDk : zero_row;
+    if (row < kTile)
+      lds_dma_b128(rowp + 8 * (v & 0x3FFu), __builtin_amdgcn_readfirstlane(base + (wave + k * NW) * 1024));
   }
 }
 
@@ -206,14 +218,28 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   // chunk_bad: the staged chunk holds an invalid slot, so every tile of it
   // takes the masked path, which also drops keys whose staged slot is -1.
   auto compute_tile = [&](const __bf16* cur, int t0, int cb, int ce, bool chunk_bad) {
-    // ---- partial S^T[key][row] over this half's 9 k-steps
+    // ---- partial S^T[key][row] over this half's 9 k-steps; K fragments are
+    // read kAhead steps ahead of the MFMAs that use them
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
     if (active) {
       const __bf16* kA0 = cur + offA;
+      bf16x8 kf0[kAhead + 1], kf1[kAhead + 1];
+#pragma unroll
+      for (int ks = 0; ks < kAhead; ++ks) {
+        kf0[ks] = lds_read_b128(kA0 + 32 * ks);
+        kf1[ks] = lds_read_b128(kA0 + 16 * kLdsStride + 32 * ks);
+      }
 #pragma unroll
       for (int ks = 0; ks < kHalfSteps; ++ks) {
-        s0 = mfma_16x16x32(lds_read_b128(kA0 + 32 * ks), qr[ks], s0);
-        s1 = mfma_16x16x32(lds_read_b128(kA0 + 16 * kLdsStride + 32 * ks), qr[ks], s1);
+        if (ks + kAhead < kHalfSteps) {
+          kf0[(ks + kAhead) % (kAhead + 1)] = lds_read_b128(kA0 + 32 * (ks + kAhead));
+          kf1[(ks + kAhead) % (kAhead + 1)] = lds_read_b128(kA0 + 16 * kLdsStride + 32 * (ks + kAhead));
+        }
+        s0 = mfma_16x16x32(kf0[ks % (kAhead + 1)], qr[ks], s0);
+        s1 = mfma_16x16x32(kf1[ks % (kAhead + 1)], qr[ks], s1);
+        // keep the reads where they are: left alone, the scheduler sinks
+        // them next to their MFMAs to save registers and serialises the loop
+        __builtin_amdgcn_sched_barrier(0);
       }
       spart[wave][0][lane] = s0;
       spart[wave][1][lane] = s1;
@@ -228,9 +254,10 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     while (__hip_atomic_load(&pair_seq[wave ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != seq)
       __builtin_amdgcn_s_sleep(1);
     asm volatile("" ::: "memory");
-    const int w0 = wave & ~1;  // fixed summation order: half 0 + half 1
-    s0 = spart[w0][0][lane] + spart[w0 + 1][0][lane];
-    s1 = spart[w0][1][lane] + spart[w0 + 1][1][lane];
+    // Both halves form half 0 + half 1 (addition commutes exactly), so the
+    // pair holds bitwise the same scores.
+    s0 += spart[wave ^ 1][0][lane];
+    s1 += spart[wave ^ 1][1][lane];
 
     // ---- mask + online softmax (lane holds row li, keys t0 + 16 kb + 4g + r)
     float x[8];  // raw scores; the softmax scale (> 0) is applied inside the exponent
@@ -281,8 +308,14 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
 
     // ---- O^T[dim][row] += V^T P^T over this half's 16 column blocks
     const __bf16* vT0 = cur + offV;
+    bf16x8 vf[kAhead + 1];
 #pragma unroll
-    for (int d = 0; d < kHalfBlocks; ++d) o[d] = mfma_16x16x32(v_operand(vT0, d), pv, o[d]);
+    for (int d = 0; d < kAhead; ++d) vf[d] = v_operand(vT0, d);
+#pragma unroll
+    for (int d = 0; d < kHalfBlocks; ++d) {
+      if (d + kAhead < kHalfBlocks) vf[(d + kAhead) % (kAhead + 1)] = v_operand(vT0, d + kAhead);
+      o[d] = mfma_16x16x32(vf[d % (kAhead + 1)], pv, o[d]);
+    }
   };
 
   // ---- main loop: chunks of up to kSlotChunk positions, tiles pipelined two ahead
