@@ -153,8 +153,10 @@ int choose_nsplit_impl(int batch, int q_len, int heads, int keys, int kv_dtype, 
   long key_sets;
   row_layout(batch, q_len, heads, kv_dtype, &nb, &groups, &key_sets);
   const long wgs_per_split = key_sets * groups;
-  // Aim at one workgroup per CU; never fewer than 4 tiles (128 keys) per split.
-  long s = (num_cus + wgs_per_split - 1) / wgs_per_split;
+  // One workgroup per CU at most (a split kernel workgroup fills a CU), so
+  // the grid runs in a single wave; never fewer than 4 tiles (128 keys) per
+  // split.
+  long s = std::max<long>(1, num_cus / wgs_per_split);
   const long cap = std::max<long>(1, ((long)keys + 127) / 128);
   s = std::min(s, cap);
   s = std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
@@ -212,8 +214,9 @@ int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsp
   const int seqlen_for_split = c->kernel == 1 ? std::min(maxlen, m->topk) : maxlen;
   int s = nsplit > 0 ? nsplit : choose_nsplit_impl(q->batch, q->q_len, q->heads, seqlen_for_split, kv->dtype, num_cus);
   if (s > MLA_MAX_NSPLIT) return MLA_ERR_INVALID_ARG;
-  const long grid = (long)s * c->groups;
-  if (grid > 0x7fffffffL || c->groups > 65535) return MLA_ERR_UNSUPPORTED;
+  // workgroup units of the 1-D split grid, indexed with int on the device
+  const long units = key_sets * s * c->groups;
+  if (units > 0x7fffffffL - 8) return MLA_ERR_UNSUPPORTED;
   c->a.nsplit = s;
   c->ws_bytes = mla_workspace_bytes(q->batch, q->q_len, q->heads, s);
   return MLA_OK;
@@ -243,6 +246,7 @@ void fill_args(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, 
   a.q_len = q->q_len;
   a.heads = q->heads;
   a.rows = q->q_len * q->heads;
+  a.row_groups = 1;
   a.mask_kind = m->kind;
   a.topk = m->kind == MLA_MASK_TOPK ? m->topk : 0;
   a.scale_log2 = (float)((double)q->sm_scale * 1.4426950408889634);

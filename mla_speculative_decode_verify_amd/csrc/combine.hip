@@ -24,83 +24,86 @@ constexpr int kCombThreads = 256;
 // Partials are fp16 rows of 512 columns with a power-of-two multiplier per
 // 256-column half (stored by the split kernels), plus an fp32 LSE.
 //
-// One workgroup per (sequence, query row, kCols-column slice). Phase 1 takes
-// M = max_s lse_s and the weights w_s = exp(lse_s - M): their sum is the
-// denominator, and w_s times each half's multiplier goes to LDS for the
-// numerator.
-// Phase 2 streams the partial slices: kCols / 8 lanes cover one split's
-// slice with one 16-byte load each, so a pass over the workgroup covers
-// 256 * 8 / kCols splits, and four passes are issued before any is used.
-// The per-lane sums meet in LDS. kCols = 64 suits many splits (8 splits per
-// wavefront load); kCols = 512 suits a few (a wavefront per split).
+// One workgroup per (sequence, query row, kCols-column slice); kCols / 8
+// lanes cover one split's slice with one 16-byte load each, so a pass of the
+// workgroup covers kGroups = 256 * 8 / kCols splits. Every lane first issues
+// the loads of its splits' slices (up to kMaxPer of them, kept in
+// registers) together with their LSEs and multipliers; the max LSE is found
+// while those loads are in flight, so the whole merge costs about one
+// memory round trip. Splits beyond kMaxPer per lane are handled by further
+// rounds of the same loop. kCols = 64 suits many splits (8 splits per
+// wavefront load), kCols = 512 a few (a wavefront per split).
 template <int kCols>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
-  constexpr int kLanes = kCols / 8;                     // lanes per split slice
-  constexpr int kGroups = kCombThreads / kLanes;        // splits per pass
-  constexpr int kUnroll = 4;
-  __shared__ float wnum[2][MLA_MAX_NSPLIT];  // numerator weights per 256-column half
+  constexpr int kLanes = kCols / 8;                 // lanes per split slice
+  constexpr int kGroups = kCombThreads / kLanes;    // splits per pass
+  constexpr int kMaxPer = 8;                        // splits per lane per round
   __shared__ float red[kCombThreads / 64];
   __shared__ float acc_lds[kGroups][kCols + 4];
+  __shared__ float den_lds[kGroups];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slice = blockIdx.x, row = blockIdx.y, b = blockIdx.z;
   const int S = a.nsplit, R = a.rows;
+  const int grp = tid / kLanes, cl = tid % kLanes;
+  const int half = (slice * kCols + cl * 8) / 256;
   const size_t p0 = (size_t)b * S * R + row;  // partial index of split s: p0 + s * R
+  const _Float16* po = a.part_o + p0 * kDv + slice * kCols + cl * 8;
+  const size_t sstride = (size_t)R * kDv;
 
-  // ---- phase 1: max LSE, then weights and their sum
+  // ---- max LSE over all splits (a separate, small pass: S floats)
   float mx = -INFINITY;
   for (int s = tid; s < S; s += kCombThreads) mx = fmaxf(mx, a.part_lse[p0 + (size_t)s * R]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[wave] = mx;
+
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  float den = 0.f;  // this lane's share of sum_s w_s (counted once per split: by lane cl == 0)
+  f16x8 v[kMaxPer];
+  float ls[kMaxPer], sc[kMaxPer];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      const int s = s0 + u * kGroups;
+      const bool ok = s < S;
+      const size_t p = p0 + (size_t)(ok ? s : 0) * R;
+      v[u] = ok ? *reinterpret_cast<const f16x8*>(po + (size_t)s * sstride) : f16x8{};
+      ls[u] = ok ? a.part_lse[p] : -INFINITY;
+      sc[u] = ok ? a.part_scale[p * 2 + half] : 0.f;
+    }
+  };
+  auto accumulate = [&]() {
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      const float w = ls[u] == -INFINITY ? 0.f : fast_exp2((ls[u] - mx) * kLog2e);  // mx > -inf whenever ls is
+      if (cl == 0) den += w;
+      const float ws = w * sc[u];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(ws, (float)v[u][j], acc[j]);
+    }
+  };
+  // first round's loads are issued before the barrier that publishes the
+  // max, so they fly while it is reduced; every thread reaches the barrier
+  load_round(grp);
   __syncthreads();
   mx = red[0];
 #pragma unroll
   for (int w = 1; w < kCombThreads / 64; ++w) mx = fmaxf(mx, red[w]);
-  __syncthreads();  // red is reused below
-  float den = 0.f;
-  for (int s = tid; s < S; s += kCombThreads) {
-    const size_t p = p0 + (size_t)s * R;
-    const float ls = a.part_lse[p];
-    const float w = ls == -INFINITY ? 0.f : fast_exp2((ls - mx) * kLog2e);  // mx > -inf whenever ls is
-    den += w;
-    wnum[0][s] = w * a.part_scale[p * 2];
-    wnum[1][s] = w * a.part_scale[p * 2 + 1];
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-  if (lane == 0) red[wave] = den;
-  __syncthreads();
-  den = red[0];
-#pragma unroll
-  for (int w = 1; w < kCombThreads / 64; ++w) den += red[w];
-
-  // ---- phase 2: weighted sum of the partial slices
-  const int grp = tid / kLanes, cl = tid % kLanes;
-  const int half = (slice * kCols + cl * 8) / 256;
-  const _Float16* po = a.part_o + p0 * kDv + slice * kCols + cl * 8;
-  const size_t sstride = (size_t)R * kDv;
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int s0 = grp; s0 < S; s0 += kUnroll * kGroups) {
-    f16x8 v[kUnroll];
-    float w[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int s = s0 + u * kGroups;
-      const bool ok = s < S;
-      v[u] = ok ? *reinterpret_cast<const f16x8*>(po + (size_t)s * sstride) : f16x8{};
-      w[u] = ok ? wnum[half][s] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(w[u], (float)v[u][j], acc[j]);
+  accumulate();
+  for (int s0 = grp + kMaxPer * kGroups; s0 < S; s0 += kMaxPer * kGroups) {
+    load_round(s0);
+    accumulate();
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc_lds[grp][cl * 8 + j] = acc[j];
+  if (cl == 0) den_lds[grp] = den;
   __syncthreads();
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float tot = 0.f;
+#pragma unroll 8
+  for (int gi = 0; gi < kGroups; ++gi) tot += den_lds[gi];
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
   for (int c = tid; c < kCols; c += kCombThreads) {
     float t = 0.f;
 #pragma unroll 8
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
     a.out[((size_t)b * R + row) * kDv + slice * kCols + c] = t * inv;
   }
   if (slice == 0 && tid == 0 && a.lse)
-    a.lse[(size_t)b * R + row] = den > 0.f ? mx + fast_log2(den) * kLn2 : -INFINITY;
+    a.lse[(size_t)b * R + row] = tot > 0.f ? mx + fast_log2(tot) * kLn2 : -INFINITY;
 }
 
 // One thread per (sequence, draft): walk the parent chain to the root.

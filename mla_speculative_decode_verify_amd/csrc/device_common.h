@@ -76,4 +76,21 @@ __device__ __forceinline__ void flag_error(unsigned* err, unsigned bits) {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// XCD-aware work order for a 1-D grid of 8 * C workgroups (C = ceil(units /
+// 8)). The hardware hands consecutive workgroup ids to the 8 XCDs in turn,
+// so id L runs on XCD L % 8. Unit j = (L % 8) * C + L / 8 gives every XCD a
+// contiguous range of units: the row groups of one KV split (numbered
+// consecutively by the caller) then run on the same XCD at about the same
+// time and share its L2 for the cache rows they all read. Ids whose unit is
+// >= `units` have no work. Only locality depends on the dispatch order;
+// every unit is covered exactly once whatever it is.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_unit(int units) {
+  const int L = blockIdx.x;
+  const int C = gridDim.x / kXcds;
+  const int j = (L % kXcds) * C + L / kXcds;
+  return j < units ? j : -1;
+}
+inline unsigned xcd_grid(long units) { return (unsigned)(((units + kXcds - 1) / kXcds) * kXcds); }
+
 }  // namespace mla

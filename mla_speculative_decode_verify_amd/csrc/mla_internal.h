@@ -33,6 +33,7 @@ struct Args {
   int slot_stride;
   int batch, q_len, heads, rows;  // rows = q_len * heads
   int nsplit;
+  int row_groups;           // workgroups along the row axis (set at launch)
   int mask_kind;
   int topk;
   float scale_log2;         // sm_scale * log2(e)

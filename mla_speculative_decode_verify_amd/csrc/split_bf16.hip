@@ -152,7 +152,11 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int half = wave & 1, blk = wave >> 1;
-  const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  // unit = (b * nsplit + split) * row_groups + grp, in XCD-aware order
+  const int G = a.row_groups;
+  const int unit = xcd_unit(a.batch * a.nsplit * G);
+  if (unit < 0) return;  // padding workgroup: uniform exit before any barrier
+  const int grp = unit % G, split = (unit / G) % a.nsplit, b = unit / (G * a.nsplit);
   const int S = a.nsplit, R = a.rows;
   const bool leader = (tid == 0) && (split == 0) && (grp == 0);
 
@@ -377,8 +381,10 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
 
 template <int NB>
 hipError_t launch_nb(const Args& a, int row_groups, hipStream_t stream) {
-  dim3 grid(a.nsplit, row_groups, a.batch);
-  hipLaunchKernelGGL(split_bf16_kernel<NB>, grid, dim3(NB * 128), 0, stream, a);
+  Args b = a;
+  b.row_groups = row_groups;
+  const long units = (long)a.batch * a.nsplit * row_groups;
+  hipLaunchKernelGGL(split_bf16_kernel<NB>, dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -159,8 +159,13 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int half = wave & 1, blk = wave >> 1;
-  const int split = blockIdx.x, grp = blockIdx.y;
-  const int b = blockIdx.z / a.q_len, qi = blockIdx.z - b * a.q_len;
+  // unit = (z * nsplit + split) * row_groups + grp with z = b * q_len + qi,
+  // in XCD-aware order
+  const int G = a.row_groups;
+  const int unit = xcd_unit(a.batch * a.q_len * a.nsplit * G);
+  if (unit < 0) return;  // padding workgroup: uniform exit before any barrier
+  const int grp = unit % G, split = (unit / G) % a.nsplit, z = unit / (G * a.nsplit);
+  const int b = z / a.q_len, qi = z - b * a.q_len;
   const int S = a.nsplit, H = a.heads, R = a.rows;
 
   int n = a.seq_lens[b];
@@ -354,8 +359,10 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
 
 template <int NB>
 hipError_t launch_nb(const Args& a, int row_groups, hipStream_t stream) {
-  dim3 grid(a.nsplit, row_groups, a.batch * a.q_len);
-  hipLaunchKernelGGL(split_fp8_topk_kernel<NB>, grid, dim3(NB * 128), 0, stream, a);
+  Args b = a;
+  b.row_groups = row_groups;
+  const long units = (long)a.batch * a.q_len * a.nsplit * row_groups;
+  hipLaunchKernelGGL(split_fp8_topk_kernel<NB>, dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
   return hipGetLastError();
 }
 

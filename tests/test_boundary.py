@@ -104,7 +104,7 @@ def test_choose_nsplit_rules(L):
     # one tensor-parallel rank's share: H=8, q_len 9 -> 72 rows, one row group
     assert B.choose_nsplit(1, 9, 8, 65545, num_cus=256) == 256
     assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 129      # capped: >= 128 keys per split
-    assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 29       # 9 row groups of 64 rows
+    assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 28       # 9 row groups: 252 workgroups, one wave
     assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 1
     assert B.choose_nsplit(32, 1, 64, 2048, kv_dtype=B.MLA_KV_FP8_E4M3, num_cus=256) == 8
     for args in [(0, 9, 8, 10, 0, 256), (1, 9, 8, -1, 0, 256), (1, 9, 8, 10, 5, 256), (1, 9, 8, 10, 0, 0)]:
