@@ -268,7 +268,8 @@ int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const i
   if (c.a.nsplit > 1) {
     void* ws = nullptr;
     if ((st = workspace(dev, stream, c.ws_bytes, &ws)) != MLA_OK) return st;
-    // [fp16 O: P x 512][fp32 LSE: P][fp32 scale: P x 2], P = batch * nsplit * rows
+    // [fp16 O: P x 512][fp32 LSE: P][fp32 scale: P x 2], P = batch * nsplit * rows;
+    // O is split-major per sequence, LSE and scales row-major (splits contiguous)
     const size_t P = (size_t)q->batch * c.a.nsplit * c.a.rows;
     char* base = static_cast<char*>(ws);
     c.a.part_o = reinterpret_cast<_Float16*>(base);

@@ -32,7 +32,7 @@ constexpr int kCombThreads = 256;
 // while those loads are in flight, so the whole merge costs about one
 // memory round trip. Splits beyond kMaxPer per lane are handled by further
 // rounds of the same loop. kCols = 64 suits many splits (8 splits per
-// wavefront load), kCols = 512 a few (a wavefront per split).
+// wavefront load), kCols = 512 up to 32 (a wavefront per split).
 template <int kCols>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   constexpr int kLanes = kCols / 8;                 // lanes per split slice
@@ -46,13 +46,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   const int S = a.nsplit, R = a.rows;
   const int grp = tid / kLanes, cl = tid % kLanes;
   const int half = (slice * kCols + cl * 8) / 256;
-  const size_t p0 = (size_t)b * S * R + row;  // partial index of split s: p0 + s * R
+  const size_t p0 = (size_t)b * S * R + row;  // partial output of split s: row p0 + s * R
+  const size_t q0 = ((size_t)b * R + row) * S;  // its LSE / scales: q0 + s (splits contiguous)
   const _Float16* po = a.part_o + p0 * kDv + slice * kCols + cl * 8;
   const size_t sstride = (size_t)R * kDv;
 
   // ---- max LSE over all splits (a separate, small pass: S floats)
   float mx = -INFINITY;
-  for (int s = tid; s < S; s += kCombThreads) mx = fmaxf(mx, a.part_lse[p0 + (size_t)s * R]);
+  for (int s = tid; s < S; s += kCombThreads) mx = fmaxf(mx, a.part_lse[q0 + s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[wave] = mx;
@@ -68,10 +69,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
     for (int u = 0; u < kMaxPer; ++u) {
       const int s = s0 + u * kGroups;
       const bool ok = s < S;
-      const size_t p = p0 + (size_t)(ok ? s : 0) * R;
+      const size_t q = q0 + (ok ? s : 0);
       v[u] = ok ? *reinterpret_cast<const f16x8*>(po + (size_t)s * sstride) : f16x8{};
-      ls[u] = ok ? a.part_lse[p] : -INFINITY;
-      sc[u] = ok ? a.part_scale[p * 2 + half] : 0.f;
+      ls[u] = ok ? a.part_lse[q] : -INFINITY;
+      sc[u] = ok ? a.part_scale[q * 2 + half] : 0.f;
     }
   };
   auto accumulate = [&]() {
@@ -144,7 +145,7 @@ __global__ void tree_mask_kernel(const int32_t* parents, int batch, int q_len, u
 }  // namespace
 
 hipError_t launch_combine(const Args& a, hipStream_t stream) {
-  if (a.nsplit <= 16) {
+  if (a.nsplit <= 32) {
     hipLaunchKernelGGL(combine_kernel<kDv>, dim3(1, a.rows, a.batch), dim3(kCombThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(combine_kernel<64>, dim3(kDv / 64, a.rows, a.batch), dim3(kCombThreads), 0, stream, a);

@@ -25,8 +25,8 @@ struct Args {
   float* out;               // [batch, rows, 512]
   float* lse;               // [batch, rows] or nullptr
   _Float16* part_o;         // [batch, nsplit, rows, 512] fp16, times part_scale per 256-column half
-  float* part_lse;          // [batch, nsplit, rows]
-  float* part_scale;        // [batch, nsplit, rows, 2] power-of-two multipliers of part_o
+  float* part_lse;          // [batch, rows, nsplit]
+  float* part_scale;        // [batch, rows, nsplit, 2] power-of-two multipliers of part_o
   unsigned* err;            // device error flag word
   const void* zero_row;     // >= 1152 zero bytes, read in place of masked / invalid cache rows
   int64_t pool_rows;

@@ -201,7 +201,8 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
 #pragma unroll
     for (int ks = 0; ks < kHalfSteps; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
   }
-  wait_vmcnt<0>();  // queries in registers before any gather is in flight
+  // No wait here: the query loads retire while the slot chunk is staged, and
+  // the wait for the staged slots (issued after them) covers them too.
 
   f32x4 o[kHalfBlocks];
 #pragma unroll

@@ -47,14 +47,15 @@ __device__ __forceinline__ void store_block_half(const Args& a, const f32x4* o, 
   const float down = __builtin_amdgcn_ldexpf(inv, -e);
   if (!row_ok) return;
   const size_t pr = ((size_t)b * S + split) * R + r_out;
+  const size_t pl = ((size_t)b * R + r_out) * S + split;  // LSE / scale: splits contiguous per row
   _Float16* dst = a.part_o + pr * kDv + 256 * half + 4 * g;
 #pragma unroll
   for (int d = 0; d < kBlocks; ++d) {
     const f32x4 v = o[d] * down;
     *reinterpret_cast<f16x4*>(dst + 16 * d) = __builtin_convertvector(v, f16x4);
   }
-  if (g == 0) a.part_scale[pr * 2 + half] = __builtin_amdgcn_ldexpf(1.f, e);
-  if (write_lse) a.part_lse[pr] = lse_v;
+  if (g == 0) a.part_scale[pl * 2 + half] = __builtin_amdgcn_ldexpf(1.f, e);
+  if (write_lse) a.part_lse[pl] = lse_v;
 }
 
 }  // namespace mla
