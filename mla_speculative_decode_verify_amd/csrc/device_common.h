@@ -28,18 +28,35 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// acc + sum of the 8 bf16 values, two at a time with the bf16 dot product
+// against (1, 1) (products are exact; each step rounds once in fp32).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+  return acc;
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Max / sum across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Max / sum across the four 16-lane groups (lanes l, l^16, l^32, l^48),
+// with the gfx950 lane swaps: permlane16_swap(v, v) yields, in lane l, the
+// values of lanes l and l^16 (the even 16-lane row's first), and
+// permlane32_swap(v, v) those of lanes l and l^32 (lower half first). Each
+// step combines the same two operands in the same order in every lane, so
+// all four lanes end with bitwise the same result.
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS

@@ -58,7 +58,7 @@ constexpr int kBufElems = kSegments * 64 * 8;      // one tile buffer incl. the 
 constexpr int kHalfSteps = kDk / 32 / 2;           // 9 MFMA k-steps per half
 constexpr int kHalfBlocks = kDv / 16 / 2;          // 16 output column blocks per half
 constexpr int kStages = 3;                         // LDS tile buffers (two tiles in flight)
-constexpr int kSlotChunk = 4096;                   // slot table entries staged in LDS at a time
+constexpr int kSlotChunk = 2048;                   // cache positions whose row addresses are staged in LDS at a time
 constexpr float kRescaleSlack = 8.f;
 #ifndef MLA_KAHEAD
 #define MLA_KAHEAD 2
@@ -68,53 +68,48 @@ constexpr int kAhead = MLA_KAHEAD;                 // LDS fragments read ahead o
 // Per-lane geometry of one wave's share of a tile gather. Piece p of the
 // padded tile is row p / kRowPieces, column piece p % kRowPieces; each wave
 // instruction moves 64 consecutive pieces (1 KiB) from 64 independent 16-byte
-// addresses. Computed once per kernel and packed as 16 bits per piece,
-// (row << 10) | piece column, two pieces per register; only the slot lookup
-// changes per tile.
+// addresses. Computed once per kernel, per piece, as (byte offset of the
+// piece in its cache row << 16) | (8 * tile row): the tile row indexes the
+// staged row addresses. Pieces past the tile (the tail of the last segment
+// lands in the buffer's padding, never read) use row kTile, an in-bounds
+// staged entry, so no lane needs a test.
 template <int NW>
 struct GatherPlan {
   static constexpr int kPer = (kSegments + NW - 1) / NW;
-  uint32_t packed[(kPer + 1) / 2];  // row >= kTile: past the tile
+  uint32_t packed[kPer];
   __device__ __forceinline__ GatherPlan(int wave, int lane) {
-#pragma unroll
-    for (int k = 0; k < (kPer + 1) / 2; ++k) packed[k] = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int sg = wave + k * NW;
       const int p = sg * 64 + lane;
       const bool live = sg < kSegments && p < kTilePieces;
       const int row = live ? p / kRowPieces : kTile;
-      const uint32_t v = (uint32_t)(row << 10) | (uint32_t)min(p - (p / kRowPieces) * kRowPieces, kPieces - 1);
-      packed[k / 2] |= v << (16 * (k & 1));
+      const int col = live ? min(p - row * kRowPieces, kPieces - 1) : 0;
+      packed[k] = ((uint32_t)(16 * col) << 16) | (uint32_t)(8 * row);
     }
   }
-  __device__ __forceinline__ uint32_t get(int k) const { return (packed[k / 2] >> (16 * (k & 1))) & 0xFFFFu; }
 };
 
-// Issue this wave's share of one tile's gather straight into LDS. Slots come
-// from the LDS-staged chunk (`slots_lds[key - chunk_lo]`, -1 where the slot
-// was outside the pool): rows at or past `hi`, or without a valid slot
-// (`pool_lim` = min(pool_rows, 2^31)), read the zero row instead, so a tile
-// never holds stale or poisoned data.
+// Issue this wave's share of one tile's gather straight into LDS. rows_lds
+// holds, for every position of the staged chunk and for 32 entries past its
+// end, the byte address of the cache row to read: the pool row of its slot,
+// or the zero row for positions past the split or with an invalid slot. So
+// a tile never holds stale or poisoned data, and a piece costs one LDS read
+// and one 64-bit add. `lds_base` and `wave` are wave-uniform (scalar).
 template <int NW>
-__device__ __forceinline__ void gather_tile(__bf16* buf, int wave, const GatherPlan<NW>& gp, const int* slots_lds,
-                                            int chunk_lo, int t0, int hi, uint32_t pool_lim, const __bf16* pool,
-                                            const __bf16* zero_row) {
+__device__ __forceinline__ void gather_tile(uint32_t lds_base, int wave, const GatherPlan<NW>& gp,
+                                            const char* const* rows_lds, int t_rel) {
   constexpr int kPer = GatherPlan<NW>::kPer;
-  const uint32_t base = lds_addr_of(buf);
+  const char* const* rows = rows_lds + t_rel;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     if (!(wave + k * NW < kSegments)) continue;  // wave-uniform
-    uint32_t v = gp.get(k);
-    // Opaque per tile, so the compiler recomputes the 64-bit source address
-    // instead of holding one per piece across the tile loop.
+    uint32_t v = gp.packed[k];
+    // Opaque per tile, so the compiler recomputes the source address instead
+    // of holding one 64-bit address per piece across the tile loop.
     asm volatile("" : "+v"(v));
-    const int row = (int)(v >> 10);
-    const int slot = slots_lds[min(t0 + row, hi - 1) - chunk_lo];
-    const bool ok = (t0 + row < hi) && ((uint32_t)slot < pool_lim);
-    const __bf16* rowp = ok ? pool + (size_t)(uint32_t)slot * kDk : zero_row;
-    if (row < kTile)
-      lds_dma_b128(rowp + 8 * (v & 0x3FFu), __builtin_amdgcn_readfirstlane(base + (wave + k * NW) * 1024));
+    const char* row = *reinterpret_cast<const char* const*>(reinterpret_cast<const char*>(rows) + (v & 0xFFFFu));
+    lds_dma_b128(row + (v >> 16), lds_base + (wave + k * NW) * 1024);
   }
 }
 
@@ -145,11 +140,11 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   constexpr int kWaitAhead = (kSegments / NW) < 63 ? (kSegments / NW) : 63;
   __shared__ __attribute__((aligned(16))) __bf16 kv[kStages * kBufElems];  // tile ring
   __shared__ __attribute__((aligned(16))) f32x4 spart[NW][2][64];          // partial scores per wave
-  __shared__ int slots_lds[kSlotChunk];                                    // slot table chunk
+  __shared__ const char* rows_lds[kSlotChunk + kTile];                     // cache-row addresses of the chunk
   __shared__ int pair_seq[NW];  // last tile whose partial scores each wave has published
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar wave index
   const int g = lane >> 4, li = lane & 15;
   const int half = wave & 1, blk = wave >> 1;
   // unit = (b * nsplit + split) * row_groups + grp, in XCD-aware order
@@ -179,8 +174,8 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int hi = min(n, lo + chunk);
 
   const int32_t* slot_row = a.slots + (size_t)b * a.slot_stride;
-  const __bf16* pool = static_cast<const __bf16*>(a.latent);
-  const __bf16* zero_row = static_cast<const __bf16*>(a.zero_row);
+  const char* pool = static_cast<const char*>(a.latent);
+  const char* zero_row = static_cast<const char*>(a.zero_row);
   const uint32_t pool_lim = (uint32_t)min<int64_t>(a.pool_rows, (int64_t)1 << 31);
   const GatherPlan<NW> gp(wave, lane);
 
@@ -221,7 +216,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   int seq = 0;                         // tiles processed by this workgroup
 
   // chunk_bad: the staged chunk holds an invalid slot, so every tile of it
-  // takes the masked path, which also drops keys whose staged slot is -1.
+  // takes the masked path, which also drops keys staged with the zero row.
   auto compute_tile = [&](const __bf16* cur, int t0, int cb, int ce, bool chunk_bad) {
     // ---- partial S^T[key][row] over this half's 9 k-steps; K fragments are
     // read kAhead steps ahead of the MFMAs that use them
@@ -280,7 +275,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
         const int d = j - prefix;
         const uint32_t word = d < 32 ? anc_lo : anc_hi;
         const uint32_t bit = (word >> (d & 31)) & 1u;
-        const bool slot_ok = slots_lds[min(j, ce - 1) - cb] >= 0;
+        const bool slot_ok = rows_lds[j - cb] != zero_row;
         const bool vis = (j < hi) & slot_ok & ((d < 0) | (bit != 0u));
         x[r] = vis ? x[r] : -INFINITY;
       }
@@ -305,11 +300,10 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float pf = fast_exp2(fmaf(x[r], a.scale_log2, -base));
-      const __bf16 pb = static_cast<__bf16>(pf);
-      pv[r] = pb;
+      pv[r] = static_cast<__bf16>(pf);
       l += pf;
-      lr += static_cast<float>(pb);
     }
+    lr = sum_bf16x8(pv, lr);
 
     // ---- O^T[dim][row] += V^T P^T over this half's 16 column blocks
     const __bf16* vT0 = cur + offV;
@@ -326,33 +320,32 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   // ---- main loop: chunks of up to kSlotChunk positions, tiles pipelined two ahead
   for (int cb = lo; cb < hi; cb += kSlotChunk) {
     const int ce = min(hi, cb + kSlotChunk);
-    // stage the chunk's slots: batches of 8 loads per thread in flight at once
+    // stage the chunk's row addresses (batches of 8 slot loads per thread in
+    // flight at once), plus kTile zero-row entries past its end
     bool lane_bad = false;
-    for (int i0 = 0; i0 < ce - cb; i0 += 8 * NW * 64) {
+    for (int i0 = 0; i0 < ce - cb + kTile; i0 += 8 * NW * 64) {
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * NW * 64 + tid;
-        v[u] = i < ce - cb ? slot_row[cb + i] : 0;
+        v[u] = i < ce - cb ? slot_row[cb + i] : -1;
       }
-      bool bad = false;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * NW * 64 + tid;
         const bool ok = (uint32_t)v[u] < pool_lim;
-        bad |= (i < ce - cb) && !ok;
-        if (i < ce - cb) slots_lds[i] = ok ? v[u] : -1;
+        lane_bad |= (i < ce - cb) && !ok;
+        if (i < ce - cb + kTile) rows_lds[i] = ok ? pool + (size_t)(uint32_t)v[u] * (kDk * 2) : zero_row;
       }
-      lane_bad |= bad;
     }
     bad_slot |= lane_bad;
-    // Slots visible to every wave, and whether any was invalid. No gather is
-    // in flight here (the previous chunk ended with a full drain), so the
-    // full barrier costs nothing.
+    // Row addresses visible to every wave, and whether any slot was invalid.
+    // No gather is in flight here (the previous chunk ended with a full
+    // drain), so the full barrier costs nothing.
     const bool chunk_bad = __syncthreads_or(lane_bad) != 0;
-    gather_tile<NW>(kv, wave, gp, slots_lds, cb, cb, ce, pool_lim, pool, zero_row);
-    if (cb + kTile < ce)
-      gather_tile<NW>(kv + kBufElems, wave, gp, slots_lds, cb, cb + kTile, ce, pool_lim, pool, zero_row);
+    const uint32_t kv_lds = lds_addr_of(kv);
+    gather_tile<NW>(kv_lds, wave, gp, rows_lds, 0);
+    if (cb + kTile < ce) gather_tile<NW>(kv_lds + kBufElems * 2, wave, gp, rows_lds, kTile);
     int buf = 0;
     for (int t0 = cb; t0 < ce; t0 += kTile) {
       if (t0 + kTile < ce) wait_vmcnt<kWaitAhead>();
@@ -360,8 +353,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       lds_barrier();  // tile t0 is in LDS for every wave; the buffer of tile t0 - 32 is free
       if (t0 + 2 * kTile < ce) {
         const int nb = buf == 0 ? kStages - 1 : buf - 1;
-        gather_tile<NW>(kv + nb * kBufElems, wave, gp, slots_lds, cb, t0 + 2 * kTile, ce, pool_lim, pool,
-                        zero_row);
+        gather_tile<NW>(kv_lds + nb * kBufElems * 2, wave, gp, rows_lds, t0 + 2 * kTile - cb);
       }
       compute_tile(kv + buf * kBufElems, t0, cb, ce, chunk_bad);
       ++seq;
@@ -377,7 +369,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const float ltr = group4_sum(lr);
   const float inv = ltr > 0.f ? 1.f / ltr : 0.f;
   const float lse_v = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
-  store_block_half(a, o, inv, lse_v, b, split, min(row, R - 1), half, g, row < R, half == 0 && g == 0);
+  // the tile ring is free now: 8 KiB of it per wavefront stages the stores
+  store_block_half(a, o, inv, lse_v, b, split, row0, min(16, R - row0), half, g, half == 0 && g == 0,
+                   reinterpret_cast<_Float16*>(kv) + wave * 4096);
 }
 
 template <int NB>

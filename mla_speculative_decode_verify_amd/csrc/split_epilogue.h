@@ -20,13 +20,21 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Lane (g, li) holds o[d][r] (d < 16) = unnormalised output column
 // 256 half + 16 d + 4 g + r of block row li; `inv` normalises it.
-// All 64 lanes must call this (it reduces across lanes); `row_ok` says
-// whether row li exists. `r_out` is the row index within the sequence.
+// All 64 lanes must call this (it reduces across lanes). The block's rows
+// are r_first .. r_first + n_valid - 1 within the sequence (n_valid <= 16),
+// so lane li's row exists iff li < n_valid.
+// `stage` is 8 KiB of LDS owned by this wavefront alone (free after the
+// tile loop): fp16 partials are transposed through it so that every store
+// instruction writes two whole 512-byte row halves instead of 32-byte
+// pieces of 16 rows.
 __device__ __forceinline__ void store_block_half(const Args& a, const f32x4* o, float inv, float lse_v,
-                                                 int b, int split, int r_out, int half, int g, bool row_ok,
-                                                 bool write_lse) {
+                                                 int b, int split, int r_first, int n_valid, int half, int g,
+                                                 bool write_lse, _Float16* stage) {
   constexpr int kBlocks = kDv / 32;  // 16 column blocks of 16 per half
   const int S = a.nsplit, R = a.rows;
+  const int lane = (int)__lane_id(), li = lane & 15;
+  const bool row_ok = li < n_valid;
+  const int r_out = r_first + li;
   if (S == 1) {
     if (!row_ok) return;
     float* dst = a.out + ((size_t)b * R + r_out) * kDv + 256 * half + 4 * g;
@@ -45,15 +53,28 @@ __device__ __forceinline__ void store_block_half(const Args& a, const f32x4* o, 
   const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127;
   const int e = min(max(ex - 14, -126), 113);
   const float down = __builtin_amdgcn_ldexpf(inv, -e);
-  if (!row_ok) return;
-  const size_t pr = ((size_t)b * S + split) * R + r_out;
-  const size_t pl = ((size_t)b * R + r_out) * S + split;  // LSE / scale: splits contiguous per row
-  _Float16* dst = a.part_o + pr * kDv + 256 * half + 4 * g;
+  // stage[row li][256 columns] in fp16, then 16-byte pieces row-major
 #pragma unroll
   for (int d = 0; d < kBlocks; ++d) {
     const f32x4 v = o[d] * down;
-    *reinterpret_cast<f16x4*>(dst + 16 * d) = __builtin_convertvector(v, f16x4);
+    *reinterpret_cast<f16x4*>(stage + li * 256 + 16 * d + 4 * g) = __builtin_convertvector(v, f16x4);
   }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = lane + 64 * i;       // 16-byte piece: row q / 32, column piece q % 32
+    const int rr = q >> 5, cp = q & 31;
+    const f32x4 piece = *reinterpret_cast<const f32x4*>(stage + rr * 256 + 8 * cp);
+    if (rr < n_valid) {
+      const size_t pr = ((size_t)b * S + split) * R + r_first + rr;
+      // streaming store: the partials are read once, by the merge kernel
+      __builtin_nontemporal_store(piece, reinterpret_cast<f32x4*>(a.part_o + pr * kDv + 256 * half + 8 * cp));
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // the stage is reused by the next call
+  if (!row_ok) return;
+  const size_t pl = ((size_t)b * R + r_out) * S + split;  // LSE / scale: splits contiguous per row
   if (g == 0) a.part_scale[pl * 2 + half] = __builtin_amdgcn_ldexpf(1.f, e);
   if (write_lse) a.part_lse[pl] = lse_v;
 }
