@@ -43,6 +43,7 @@ constexpr int kLatPieces = kDv / 8;                 // 8-byte fp8 pieces per lat
 constexpr int kRopePieces = kDrope / 8;             // 16-byte bf16 pieces per rope row (8)
 constexpr int kChunk = 4096;                        // top-k entries staged in LDS at a time
 constexpr float kRescaleSlack = 8.f;
+constexpr int kAhead = 2;                           // LDS fragments read ahead of their MFMAs
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -218,42 +219,51 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
 
   auto compute_tile = [&](const __bf16* cur, const float* sc, const float* isc, const float* bias) {
     if (!active) return;
-    // ---- partial scores over this half's k-steps: latent and rope kept apart
+    // ---- partial scores over this half's k-steps: latent and rope kept
+    // apart. K fragments are read kAhead steps ahead of their MFMAs; the
+    // scheduling barrier keeps the reads from sinking next to their use.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, r0 = s0, r1 = s0;
     const __bf16* kA0 = cur + offA;
-    if (half == 0) {
+    bf16x8 kf0[kAhead + 1], kf1[kAhead + 1];
 #pragma unroll
-      for (int ks = 0; ks < kHalfSteps; ++ks) {
-        s0 = mfma_16x16x32(lds_read_b128(kA0 + 32 * ks), qr[ks], s0);
-        s1 = mfma_16x16x32(lds_read_b128(kA0 + 16 * kLdsStride + 32 * ks), qr[ks], s1);
-      }
-    } else {
+    for (int ks = 0; ks < kAhead; ++ks) {
+      kf0[ks] = lds_read_b128(kA0 + 32 * ks);
+      kf1[ks] = lds_read_b128(kA0 + 16 * kLdsStride + 32 * ks);
+    }
+    const bool rope_steps = half == 1;  // half 1's last two k-steps are the rope
 #pragma unroll
-      for (int ks = 0; ks < kLatHalf1; ++ks) {
-        s0 = mfma_16x16x32(lds_read_b128(kA0 + 32 * ks), qr[ks], s0);
-        s1 = mfma_16x16x32(lds_read_b128(kA0 + 16 * kLdsStride + 32 * ks), qr[ks], s1);
+    for (int ks = 0; ks < kHalfSteps; ++ks) {
+      if (ks + kAhead < kHalfSteps) {
+        kf0[(ks + kAhead) % (kAhead + 1)] = lds_read_b128(kA0 + 32 * (ks + kAhead));
+        kf1[(ks + kAhead) % (kAhead + 1)] = lds_read_b128(kA0 + 16 * kLdsStride + 32 * (ks + kAhead));
       }
-#pragma unroll
-      for (int ks = kLatHalf1; ks < kHalfSteps; ++ks) {
-        r0 = mfma_16x16x32(lds_read_b128(kA0 + 32 * ks), qr[ks], r0);
-        r1 = mfma_16x16x32(lds_read_b128(kA0 + 16 * kLdsStride + 32 * ks), qr[ks], r1);
+      const bf16x8 k0 = kf0[ks % (kAhead + 1)], k1 = kf1[ks % (kAhead + 1)];
+      if (ks >= kLatHalf1 && rope_steps) {
+        r0 = mfma_16x16x32(k0, qr[ks], r0);
+        r1 = mfma_16x16x32(k1, qr[ks], r1);
+      } else {
+        s0 = mfma_16x16x32(k0, qr[ks], s0);
+        s1 = mfma_16x16x32(k1, qr[ks], s1);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // lane holds keys 16 kb + 4 g + r (r = 0..3) of row li
     const f32x4 sc0 = *reinterpret_cast<const f32x4*>(sc + 4 * g);
     const f32x4 sc1 = *reinterpret_cast<const f32x4*>(sc + 16 + 4 * g);
-    spart[wave][0][lane] = sc0 * s0 + r0;
-    spart[wave][1][lane] = sc1 * s1 + r1;
+    const f32x4 own0 = sc0 * s0 + r0, own1 = sc1 * s1 + r1;
+    spart[wave][0][lane] = own0;
+    spart[wave][1][lane] = own1;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial stored before the flag
     if (lane == 0) __hip_atomic_store(&pair_seq[wave], seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     while (__hip_atomic_load(&pair_seq[wave ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != seq)
       __builtin_amdgcn_s_sleep(1);
     asm volatile("" ::: "memory");
-    const int w0 = wave & ~1;  // fixed summation order: half 0 + half 1
+    // own + partner: addition commutes exactly, so both halves hold bitwise
+    // the same sums
     const f32x4 b0 = *reinterpret_cast<const f32x4*>(bias + 4 * g);
     const f32x4 b1 = *reinterpret_cast<const f32x4*>(bias + 16 + 4 * g);
-    const f32x4 x0 = (spart[w0][0][lane] + spart[w0 + 1][0][lane]) + b0;
-    const f32x4 x1 = (spart[w0][1][lane] + spart[w0 + 1][1][lane]) + b1;
+    const f32x4 x0 = (own0 + spart[wave ^ 1][0][lane]) + b0;
+    const f32x4 x1 = (own1 + spart[wave ^ 1][1][lane]) + b1;
     const f32x4 is0 = *reinterpret_cast<const f32x4*>(isc + 4 * g);
     const f32x4 is1 = *reinterpret_cast<const f32x4*>(isc + 16 + 4 * g);
     float x[8], s[8], is[8];
@@ -294,8 +304,14 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
 
     // ---- O^T[dim][row] += V^T P^T over this half's 16 column blocks
     const __bf16* vT0 = cur + offV;
+    bf16x8 vf[kAhead + 1];
 #pragma unroll
-    for (int d = 0; d < kHalfBlocks; ++d) o[d] = mfma_16x16x32(v_operand(vT0, d), pv, o[d]);
+    for (int d = 0; d < kAhead; ++d) vf[d] = v_operand(vT0, d);
+#pragma unroll
+    for (int d = 0; d < kHalfBlocks; ++d) {
+      if (d + kAhead < kHalfBlocks) vf[(d + kAhead) % (kAhead + 1)] = v_operand(vT0, d + kAhead);
+      o[d] = mfma_16x16x32(vf[d % (kAhead + 1)], pv, o[d]);
+    }
   };
 
   TileRegs<NW> regs;
