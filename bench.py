@@ -268,8 +268,8 @@ def main():
 
 
 KERNEL_SOURCES = {
-    "verify": ("split_bf16.hip", "device_common.h", "mla_internal.h"),
-    "sparse": ("split_fp8.hip", "device_common.h", "mla_internal.h"),
+    "verify": ("split_bf16.hip", "split_epilogue.h", "device_common.h", "mla_internal.h"),
+    "sparse": ("split_fp8.hip", "split_epilogue.h", "device_common.h", "mla_internal.h"),
 }
 
 

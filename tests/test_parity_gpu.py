@@ -114,16 +114,30 @@ def test_tree_mask_device_bit_exact():
     assert B.device_error() == 0
 
 
-def test_split_and_combine_stages_equal_full_call():
-    w = I.workload("c1")
+@pytest.mark.parametrize("name,nsplit", [
+    ("c1", 4),        # few splits: whole-row merge units
+    ("c3_16k", 0),    # library's choice: many splits, 64-column merge units
+    ("c3_64k", 0),
+    ("c3_64k", 40),
+    ("c2", 0),
+])
+def test_split_and_combine_stages_equal_full_call(name, nsplit):
+    # The two entry points of the split and the merge, called in turn, give
+    # the full call's result bit for bit, for whole-row and 64-column merge
+    # units alike; a repeated full call reproduces it.
+    w = I.workload(name)
     d = DeviceInputs(w)
-    o1, l1 = d.run(nsplit=4)
+    _log(f"[stages] {name} nsplit={nsplit}")
+    o1, l1 = d.run(nsplit=nsplit)
     o2 = torch.empty_like(o1)
     l2 = torch.empty_like(l1)
-    d.run(nsplit=4, stage="split", out=o2, lse=l2)
-    d.run(nsplit=4, stage="combine", out=o2, lse=l2)
+    d.run(nsplit=nsplit, stage="split", out=o2, lse=l2)
+    d.run(nsplit=nsplit, stage="combine", out=o2, lse=l2)
+    o3, l3 = d.run(nsplit=nsplit)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    assert B.device_error() == 0
 
 
 @pytest.mark.parametrize("factor", [1.0e5, 1.0e-4])

@@ -140,3 +140,22 @@ def test_verify_bad_slot_is_masked_and_flagged():
         torch.cuda.synchronize()
         compare(out, lse, ref_out, ref_lse, f"badslot nsplit={ns}")
         assert B.device_error() == B.MLA_DEVERR_SLOT_RANGE
+
+
+@pytest.mark.parametrize("nsplit", [3, 8, 40, 0])
+def test_sparse_stages_equal_full_call(nsplit):
+    # Split and merge entry points called in turn equal the full call bit
+    # for bit (4 key sets of 64 heads), and a repeated call reproduces it.
+    w = I.make_sparse("stages", batch=2, q_len=2, heads=64, prefix=3000, topk=2048, seed=75)
+    d = DeviceInputs(w)
+    print(f"[sparse stages] nsplit={nsplit}", flush=True)
+    o1, l1 = d.run(nsplit=nsplit)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    d.run(nsplit=nsplit, stage="split", out=o2, lse=l2)
+    d.run(nsplit=nsplit, stage="combine", out=o2, lse=l2)
+    o3, l3 = d.run(nsplit=nsplit)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    assert B.device_error() == 0
