@@ -242,6 +242,7 @@ void fill_args(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, 
   a.zero_row = nullptr;
   a.pool_rows = kv->pool_rows;
   a.slot_stride = kv->slot_stride;
+  a.len_hint = kv->max_seq_len > 0 ? kv->max_seq_len : kv->slot_stride;
   a.batch = q->batch;
   a.q_len = q->q_len;
   a.heads = q->heads;

@@ -31,6 +31,9 @@ struct Args {
   const void* zero_row;     // >= 1152 zero bytes, read in place of masked / invalid cache rows
   int64_t pool_rows;
   int slot_stride;
+  int len_hint;             // host-side bound of seq_lens (max_seq_len, else slot_stride): the
+                            // split kernels start loading the slots of the split this implies
+                            // before the true length arrives, and keep them if it matches
   int batch, q_len, heads, rows;  // rows = q_len * heads
   int nsplit;
   int row_groups;           // workgroups along the row axis (set at launch)

@@ -154,6 +154,21 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int grp = unit % G, split = (unit / G) % a.nsplit, b = unit / (G * a.nsplit);
   const int S = a.nsplit, R = a.rows;
   const bool leader = (tid == 0) && (split == 0) && (grp == 0);
+  const int32_t* slot_row = a.slots + (size_t)b * a.slot_stride;
+
+  // ---- first batch of slot loads, issued before the sequence length is
+  // known: they assume the split range that the host's length bound implies
+  // and are used only if the true range turns out the same, so the slot
+  // loads no longer wait behind the length load
+  constexpr int kBatch = NW * 64;  // slot loads per staging pass and unroll step
+  const int chunk_h = (a.len_hint + S - 1) / S;
+  const int lo_h = min(a.len_hint, split * chunk_h);
+  int v_h[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = u * kBatch + tid;
+    v_h[u] = (i < min(chunk_h, kSlotChunk) && lo_h + i < a.slot_stride) ? slot_row[lo_h + i] : -1;
+  }
 
   // ---- sequence bounds and this split's key range
   int n = a.seq_lens[b];
@@ -172,8 +187,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int chunk = (n + S - 1) / S;
   const int lo = min(n, split * chunk);
   const int hi = min(n, lo + chunk);
-
-  const int32_t* slot_row = a.slots + (size_t)b * a.slot_stride;
+  const bool hint_ok = chunk == chunk_h && lo == lo_h;  // the early loads are this split's slots
   const char* pool = static_cast<const char*>(a.latent);
   const char* zero_row = static_cast<const char*>(a.zero_row);
   const uint32_t pool_lim = (uint32_t)min<int64_t>(a.pool_rows, (int64_t)1 << 31);
@@ -323,16 +337,17 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     // stage the chunk's row addresses (batches of 8 slot loads per thread in
     // flight at once), plus kTile zero-row entries past its end
     bool lane_bad = false;
-    for (int i0 = 0; i0 < ce - cb + kTile; i0 += 8 * NW * 64) {
+    for (int i0 = 0; i0 < ce - cb + kTile; i0 += 8 * kBatch) {
       int v[8];
+      const bool early = hint_ok && cb == lo && i0 == 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * NW * 64 + tid;
-        v[u] = i < ce - cb ? slot_row[cb + i] : -1;
+        const int i = i0 + u * kBatch + tid;
+        v[u] = i < ce - cb ? (early ? v_h[u] : slot_row[cb + i]) : -1;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * NW * 64 + tid;
+        const int i = i0 + u * kBatch + tid;
         const bool ok = (uint32_t)v[u] < pool_lim;
         lane_bad |= (i < ce - cb) && !ok;
         if (i < ce - cb + kTile) rows_lds[i] = ok ? pool + (size_t)(uint32_t)v[u] * (kDk * 2) : zero_row;
