@@ -29,7 +29,9 @@
  * The KV axis of each sequence is cut into nsplit contiguous chunks of
  * ceil(N / nsplit) positions ("How One Environment Variable Unlocked 3x
  * Throughput", section "The Occupancy Revelation": the split count NSPLIT
- * multiplies the grid); each chunk produces a normalised partial output and
+ * multiplies the grid); the bf16 kernel rounds a chunk up to whole
+ * 32-position tiles, so trailing chunks may be shorter or empty. Each chunk
+ * produces a normalised partial output and
  * its LSE, and a second kernel merges them by log-sum-exp weights. The merge
  * is exact in real arithmetic, so results do not depend on nsplit beyond
  * floating-point rounding.
@@ -177,7 +179,9 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
 
 /* Split count the library picks when nsplit <= 0: a pure function of the
  * shape and the CU count, so it is deterministic and safe under graph
- * capture. max_seq_len is the longest sequence for a bf16 cache and the
+ * capture. At most one split-kernel workgroup per CU and at least 128
+ * positions per split; for a bf16 cache, the fewest splits that keep the
+ * largest per-split count of 32-position tiles. max_seq_len is the longest sequence for a bf16 cache and the
  * top-k list length for an fp8 cache (each query's list is split). ("How One Environment Variable Unlocked 3x Throughput", section
  * "The Occupancy Revelation": a small per-rank head count shrinks the grid
  * until the machine starves, and more splits refill it.) */

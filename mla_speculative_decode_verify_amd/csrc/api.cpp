@@ -159,6 +159,14 @@ int choose_nsplit_impl(int batch, int q_len, int heads, int keys, int kv_dtype, 
   long s = std::max<long>(1, num_cus / wgs_per_split);
   const long cap = std::max<long>(1, ((long)keys + 127) / 128);
   s = std::min(s, cap);
+  if (kv_dtype == MLA_KV_BF16) {
+    // The verify kernel gives each split whole 32-position tiles, so the
+    // slowest split runs ceil(tiles / s) of them: take the fewest splits
+    // with that same maximum (fewer partials to write and merge).
+    const long tiles = std::max<long>(1, ((long)keys + 31) / 32);
+    const long per = (tiles + s - 1) / s;
+    s = (tiles + per - 1) / per;
+  }
   s = std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
   return (int)s;
 }

@@ -31,7 +31,7 @@
 // The gathers are issued as inline assembly and counted by hand: the compiler
 // would otherwise drain the whole load queue before every LDS read of a tile
 // (it cannot tell which buffer an in-flight global-to-LDS load writes). The
-// slot table of each chunk of up to 4096 positions is staged in LDS first, so
+// slot table of each chunk of up to 2048 positions is staged in LDS first, so
 // the only vector-memory operations inside the tile loop are the gathers.
 //
 // The running max is updated lazily: the exponent base only moves (and the
@@ -64,6 +64,13 @@ constexpr float kRescaleSlack = 8.f;
 #define MLA_KAHEAD 2
 #endif
 constexpr int kAhead = MLA_KAHEAD;                 // LDS fragments read ahead of their MFMAs
+#ifndef MLA_V_EARLY
+#define MLA_V_EARLY 0
+#endif
+#ifndef MLA_VAHEAD
+#define MLA_VAHEAD MLA_KAHEAD
+#endif
+constexpr int kVAhead = MLA_VAHEAD;                // V fragments read ahead of their MFMAs
 
 // Per-lane geometry of one wave's share of a tile gather. Piece p of the
 // padded tile is row p / kRowPieces, column piece p % kRowPieces; each wave
@@ -113,6 +120,11 @@ __device__ __forceinline__ void gather_tile(uint32_t lds_base, int wave, const G
   }
 }
 
+// Positions per split: n / S rounded up to whole tiles, so that no split
+// pays a full tile for a few leftover positions (trailing splits may be
+// empty).
+__device__ __forceinline__ int split_chunk(int n, int S) { return ((n + S - 1) / S + kTile - 1) / kTile * kTile; }
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
@@ -161,7 +173,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   // and are used only if the true range turns out the same, so the slot
   // loads no longer wait behind the length load
   constexpr int kBatch = NW * 64;  // slot loads per staging pass and unroll step
-  const int chunk_h = (a.len_hint + S - 1) / S;
+  const int chunk_h = split_chunk(a.len_hint, S);
   const int lo_h = min(a.len_hint, split * chunk_h);
   int v_h[8];
 #pragma unroll
@@ -184,7 +196,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       prefix = 0;
     }
   }
-  const int chunk = (n + S - 1) / S;
+  const int chunk = split_chunk(n, S);
   const int lo = min(n, split * chunk);
   const int hi = min(n, lo + chunk);
   const bool hint_ok = chunk == chunk_h && lo == lo_h;  // the early loads are this split's slots
@@ -235,6 +247,8 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     // ---- partial S^T[key][row] over this half's 9 k-steps; K fragments are
     // read kAhead steps ahead of the MFMAs that use them
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    const __bf16* vT0 = cur + offV;
+    bf16x8 vf[kVAhead + 1];
     if (active) {
       const __bf16* kA0 = cur + offA;
       bf16x8 kf0[kAhead + 1], kf1[kAhead + 1];
@@ -257,6 +271,13 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       }
       spart[wave][0][lane] = s0;
       spart[wave][1][lane] = s1;
+      if (MLA_V_EARLY) {
+        // the first V fragments do not depend on the scores: their LDS
+        // latency overlaps the score exchange and the softmax
+#pragma unroll
+        for (int d = 0; d < kVAhead; ++d) vf[d] = v_operand(vT0, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (!active) return;
     // Publish this wave's partial, then wait for the partner wave's: only the
@@ -320,14 +341,14 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     lr = sum_bf16x8(pv, lr);
 
     // ---- O^T[dim][row] += V^T P^T over this half's 16 column blocks
-    const __bf16* vT0 = cur + offV;
-    bf16x8 vf[kAhead + 1];
+    if (!MLA_V_EARLY) {
 #pragma unroll
-    for (int d = 0; d < kAhead; ++d) vf[d] = v_operand(vT0, d);
+      for (int d = 0; d < kVAhead; ++d) vf[d] = v_operand(vT0, d);
+    }
 #pragma unroll
     for (int d = 0; d < kHalfBlocks; ++d) {
-      if (d + kAhead < kHalfBlocks) vf[(d + kAhead) % (kAhead + 1)] = v_operand(vT0, d + kAhead);
-      o[d] = mfma_16x16x32(vf[d % (kAhead + 1)], pv, o[d]);
+      if (d + kVAhead < kHalfBlocks) vf[(d + kVAhead) % (kVAhead + 1)] = v_operand(vT0, d + kVAhead);
+      o[d] = mfma_16x16x32(vf[d % (kVAhead + 1)], pv, o[d]);
     }
   };
 
