@@ -29,8 +29,9 @@
  * The KV axis of each sequence is cut into nsplit contiguous chunks of
  * ceil(N / nsplit) positions ("How One Environment Variable Unlocked 3x
  * Throughput", section "The Occupancy Revelation": the split count NSPLIT
- * multiplies the grid); the bf16 kernel rounds a chunk up to whole
- * 32-position tiles, so trailing chunks may be shorter or empty. Each chunk
+ * multiplies the grid); the bf16 kernel instead deals the ceil(N / 32)
+ * 32-position tiles out as evenly as possible, the extra ones to the last
+ * chunks (leading chunks are empty when nsplit exceeds the tile count). Each chunk
  * produces a normalised partial output and
  * its LSE, and a second kernel merges them by log-sum-exp weights. The merge
  * is exact in real arithmetic, so results do not depend on nsplit beyond

@@ -120,10 +120,19 @@ __device__ __forceinline__ void gather_tile(uint32_t lds_base, int wave, const G
   }
 }
 
-// Positions per split: n / S rounded up to whole tiles, so that no split
-// pays a full tile for a few leftover positions (trailing splits may be
-// empty).
-__device__ __forceinline__ int split_chunk(int n, int S) { return ((n + S - 1) / S + kTile - 1) / kTile * kTile; }
+// Positions [lo, hi) of split `split` of S over n positions: the ceil(n / 32)
+// tiles are dealt out as evenly as possible, the extra ones to the last
+// splits (which also hold the sequence's final, possibly partial tile), so
+// no split pays a full tile for a few leftover positions and the splits
+// that finish first are the many with fewer tiles.
+__device__ __forceinline__ void split_range(int n, int S, int split, int& lo, int& hi) {
+  const int tiles = (n + kTile - 1) / kTile;
+  const int base = tiles / S, first_big = S - (tiles - base * S);
+  const int t0 = split * base + max(0, split - first_big);
+  const int nt = base + (split >= first_big ? 1 : 0);
+  lo = min(n, t0 * kTile);
+  hi = min(n, (t0 + nt) * kTile);
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -173,13 +182,13 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   // and are used only if the true range turns out the same, so the slot
   // loads no longer wait behind the length load
   constexpr int kBatch = NW * 64;  // slot loads per staging pass and unroll step
-  const int chunk_h = split_chunk(a.len_hint, S);
-  const int lo_h = min(a.len_hint, split * chunk_h);
+  int lo_h, hi_h;
+  split_range(a.len_hint, S, split, lo_h, hi_h);
   int v_h[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int i = u * kBatch + tid;
-    v_h[u] = (i < min(chunk_h, kSlotChunk) && lo_h + i < a.slot_stride) ? slot_row[lo_h + i] : -1;
+    v_h[u] = (i < min(hi_h - lo_h, kSlotChunk) && lo_h + i < a.slot_stride) ? slot_row[lo_h + i] : -1;
   }
 
   // ---- sequence bounds and this split's key range
@@ -196,10 +205,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       prefix = 0;
     }
   }
-  const int chunk = split_chunk(n, S);
-  const int lo = min(n, split * chunk);
-  const int hi = min(n, lo + chunk);
-  const bool hint_ok = chunk == chunk_h && lo == lo_h;  // the early loads are this split's slots
+  int lo, hi;
+  split_range(n, S, split, lo, hi);
+  const bool hint_ok = lo == lo_h && hi <= hi_h;  // the early loads hold this split's first slots
   const char* pool = static_cast<const char*>(a.latent);
   const char* zero_row = static_cast<const char*>(a.zero_row);
   const uint32_t pool_lim = (uint32_t)min<int64_t>(a.pool_rows, (int64_t)1 << 31);
