@@ -1,0 +1,54 @@
+"""Graph capture: a verify call recorded into a HIP graph (through
+torch.cuda.graph) and replayed matches the eager call bit for bit.
+
+The workspace is reserved on the capturing stream first, so the captured
+call allocates nothing; between replays the outputs are cleared eagerly and
+the device is synchronised, and every replay is checked.
+"""
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mla_speculative_decode_verify_amd import binding as B  # noqa: E402
+from mla_speculative_decode_verify_amd import inputs as I  # noqa: E402
+
+from gpu_util import DeviceInputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,nsplit", [("c1", 4), ("c3_16k", 0), ("c4", 0), ("c5", 0)])
+def test_graph_replay_matches_eager(name, nsplit):
+    w = I.workload(name)
+    d = DeviceInputs(w)
+    print(f"[graph] {name} nsplit={nsplit}", flush=True)
+    ref_o, ref_l = d.run(nsplit=nsplit)
+    torch.cuda.synchronize()
+    sparse = w.kind == "sparse"
+    p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=nsplit, mask=w.mask,
+               kv_dtype=B.MLA_KV_FP8_E4M3 if sparse else B.MLA_KV_BF16,
+               topk=w.meta["topk"] if sparse else 0)
+    s = torch.cuda.Stream()
+    B.reserve_workspace(p["workspace_bytes"], stream=s)
+    out = torch.empty_like(ref_o)
+    lse = torch.empty_like(ref_l)
+    if sparse:
+        call = B.PreparedCall(d.q, latent=d.lat, rope=d.rope, scale=d.scale, slot_table=d.slots,
+                              seq_lens=d.seq_lens, topk_idx=d.topk, sm_scale=w.sm_scale, out=out, lse=lse,
+                              nsplit=nsplit)
+    else:
+        call = B.PreparedCall(d.q, kv=d.kv, slot_table=d.slots, seq_lens=d.seq_lens, sm_scale=w.sm_scale,
+                              mask=w.mask, tree_anc=d.anc, out=out, lse=lse, nsplit=nsplit)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    assert B.device_error() == 0
