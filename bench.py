@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--nsplit", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough for > 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="verify", choices=["verify", "append"],
+                    help="append: time the draft-KV append (mla_append_kv) for the workload's shape instead")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -57,7 +59,11 @@ def describe(w):
     pre = w.meta["prefixes"]
     pre_s = str(pre[0]) if len(set(pre)) == 1 else f"{min(pre)}..{max(pre)}"
     return (f"{w.name}: batch {w.batch}, q_len {w.q_len}, H {w.heads}, prefix {pre_s}, bf16 latent, "
-            f"page_size=1 {'random' if w.meta['layout'] == 'random' else 'contiguous'} slots, {w.mask} mask")
+            f"page_size=1 {LAYOUT_WORDS[w.meta['layout']]} slots, {w.mask} mask")
+
+
+LAYOUT_WORDS = {"random": "random", "contiguous": "contiguous",
+                "sorted": "sorted (random free rows handed out in ascending order)"}
 
 
 def _replicate(host, copies, dtype=None):
@@ -186,6 +192,9 @@ def main():
     torch.cuda.set_device(0)
     B.lib()
     w = I.workload(args.workload)
+    if args.op == "append":
+        bench_append(args, w)
+        return
     if w.kind == "sparse":
         cnt = RL.sparse_counts(w.batch, w.q_len, w.heads, w.meta["topk"])
         read_bytes = w.batch * w.q_len * w.meta["topk"] * 652
@@ -265,6 +274,51 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_append(args, w):
+    """One JSON line for the draft-KV append of the workload's batch x q_len rows into its pool."""
+    import numpy as np
+    import torch
+
+    from mla_speculative_decode_verify_amd import binding as B
+
+    assert w.kind == "verify", "the append writes a bf16 pool"
+    rng = np.random.default_rng(77)
+    new = rng.integers(0, 0x7F00, size=(w.batch, w.q_len, 576)).astype(np.uint16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    kv = dev(w.pool_bits.view(np.int16)).view(torch.bfloat16)
+    new_t = dev(new.view(np.int16)).view(torch.bfloat16)
+    slots, lens = dev(w.slot_table), dev(w.seq_lens)
+    B.append_kv(kv, new_t, slots, lens)  # validates the arguments once
+    L = B.lib()
+    cargs = (kv.data_ptr(), int(kv.shape[0]), int(slots.shape[1]), new_t.data_ptr(), w.batch, w.q_len,
+             slots.data_ptr(), lens.data_ptr(), int(torch.cuda.current_stream().cuda_stream))
+    call = lambda: L.mla_append_kv(*cargs)  # noqa: E731  (no per-call Python validation)
+    us = time_calls([call], args.steps, args.warmup, rotate=False)
+    rows = w.batch * w.q_len
+    nbytes = rows * 1152 * 2 + rows * 4 + w.batch * 4
+    log(f"[bench] append {rows} rows: {us:.2f} us/call")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import mla_oracle as O
+
+        t = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.append_kv(w.pool_bits, new, w.slot_table, w.seq_lens)
+            t.append((time.perf_counter() - t0) * 1e6)
+        cpu = {"value": round(statistics.median(t), 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+               "sample": "the full append (a copy of the pool plus the row writes), median of 3"}
+    ach = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "draft-KV append µs/call", "value": round(us, 3), "unit": "us/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded bf16 bit patterns",
+        "config": {"workload": describe(w), "rows": rows},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(ach / 8000.0, 5), "traffic": None},
+        "cpu_baseline": cpu}), flush=True)
 
 
 KERNEL_SOURCES = {

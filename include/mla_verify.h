@@ -212,6 +212,26 @@ int mla_build_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* 
                         hipStream_t stream);
 int mla_build_tree_mask_host(const int32_t* parents, int batch, int q_len, uint64_t* anc_out);
 
+/* Draft-KV append: write the q_len new tokens of every sequence into a bf16
+ * latent pool (page_size = 1) before a verify call. Row i of sequence b,
+ * new_rows[b, i, :] (bf16 [batch, q_len, 576], contiguous), goes to pool row
+ * slot_table[b, seq_lens[b] - q_len + i], i.e. the draft positions that
+ * mla_verify_attn reads. ("How One Environment Variable Unlocked 3x
+ * Throughput", sections "The Central Dilemma" and "Potential Mistakes":
+ * each request's KV lives in pool slots handed out by the allocator, and
+ * whether they are contiguous decides how the gather behaves.)
+ *   latent:     device bf16 [pool_rows, 576], written in place (16-byte
+ *               aligned, like new_rows).
+ *   slot_table: device int32 [batch, slot_stride]; seq_lens: device int32
+ *               [batch] with q_len <= seq_lens[b] <= slot_stride.
+ * The target slots must be distinct (two writes to one pool row race).
+ * A sequence with an out-of-range length writes nothing and sets
+ * MLA_DEVERR_SEQ_LEN; a row whose slot is outside [0, pool_rows) is skipped
+ * and sets MLA_DEVERR_SLOT_RANGE. Enqueued on `stream`; allocates nothing
+ * but the device error flag on first use. q_len must be in [1, 64]. */
+int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* new_rows, int batch, int q_len,
+                  const int32_t* slot_table, const int32_t* seq_lens, hipStream_t stream);
+
 /* Read (and optionally clear) the current device's sticky error flags.
  * Synchronises the device. Returns the MLA_DEVERR_* bits, or a negative
  * status code. */

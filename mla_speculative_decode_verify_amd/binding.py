@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.mla_build_tree_mask.restype = ctypes.c_int
     L.mla_build_tree_mask_host.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.mla_build_tree_mask_host.restype = ctypes.c_int
+    L.mla_append_kv.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_append_kv.restype = ctypes.c_int
     L.mla_get_device_error.argtypes = [ctypes.c_int]
     L.mla_get_device_error.restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
@@ -269,6 +272,25 @@ def build_tree_mask(parents, stream=None):
     _check(lib().mla_build_tree_mask(parents.data_ptr(), B, Q, anc.data_ptr(), _stream_handle(stream)),
            "mla_build_tree_mask")
     return anc
+
+
+def append_kv(kv, new_rows, slot_table, seq_lens, stream=None):
+    """Write the drafts' latent rows (bf16 [B, Q, 576]) into the bf16 pool ``kv`` [pool_rows, 576] in place,
+    at the pool rows of positions seq_lens[b] - Q .. seq_lens[b] - 1 of each slot table row."""
+    import torch
+
+    _req(kv, torch.bfloat16, "kv")
+    _req(new_rows, torch.bfloat16, "new_rows")
+    _req(slot_table, torch.int32, "slot_table")
+    if kv.dim() != 2 or kv.shape[1] != 576 or new_rows.dim() != 3 or new_rows.shape[2] != 576:
+        raise ValueError("kv must be [pool_rows, 576] and new_rows [B, Q, 576]")
+    bsz, q_len = int(new_rows.shape[0]), int(new_rows.shape[1])
+    if slot_table.dim() != 2 or slot_table.shape[0] != bsz:
+        raise ValueError("slot_table must be [B, slot_stride]")
+    _req(seq_lens, torch.int32, "seq_lens", (bsz,))
+    _check(lib().mla_append_kv(kv.data_ptr(), int(kv.shape[0]), int(slot_table.shape[1]), new_rows.data_ptr(), bsz,
+                               q_len, slot_table.data_ptr(), seq_lens.data_ptr(), _stream_handle(stream)),
+           "mla_append_kv")
 
 
 def build_tree_mask_host(parents: np.ndarray) -> np.ndarray:

@@ -386,6 +386,24 @@ int mla_build_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* 
   return mla::launch_tree_mask(parents, batch, q_len, anc_out, err, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
+int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* new_rows, int batch, int q_len,
+                  const int32_t* slot_table, const int32_t* seq_lens, hipStream_t stream) {
+  if (!latent || !new_rows || !slot_table || !seq_lens) return MLA_ERR_INVALID_ARG;
+  if (batch < 1 || q_len < 1 || pool_rows < 1 || slot_stride < q_len) return MLA_ERR_INVALID_ARG;
+  if (q_len > MLA_MAX_Q_LEN) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(latent, 16) || !aligned(new_rows, 16) || !aligned(slot_table, 4) || !aligned(seq_lens, 4))
+    return MLA_ERR_ALIGN;
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  unsigned* err = nullptr;
+  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  return mla::launch_append(latent, pool_rows, slot_stride, new_rows, batch, q_len, slot_table, seq_lens, err,
+                            stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_LAUNCH;
+}
+
 int mla_get_device_error(int clear) {
   int dev = 0;
   int st = current_device(&dev);

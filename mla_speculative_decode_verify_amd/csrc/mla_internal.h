@@ -49,6 +49,11 @@ hipError_t launch_split_bf16(const Args& a, int blocks, int row_groups, hipStrea
 hipError_t launch_split_fp8_topk(const Args& a, int blocks, int row_groups, hipStream_t stream);
 // Log-sum-exp merge of the partials into out / lse.
 hipError_t launch_combine(const Args& a, hipStream_t stream);
+// Draft-KV append: row i of sequence b of new_rows (bf16 [batch, q_len, 576])
+// to pool row slots[b, seq_lens[b] - q_len + i].
+hipError_t launch_append(void* latent, int64_t pool_rows, int slot_stride, const void* new_rows, int batch,
+                         int q_len, const int32_t* slots, const int32_t* seq_lens, unsigned* err,
+                         hipStream_t stream);
 // Ancestor-or-self masks from parent arrays.
 hipError_t launch_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* anc, unsigned* err,
                             hipStream_t stream);

@@ -96,7 +96,8 @@ def make_verify(name: str, *, batch: int, q_len: int, heads: int, prefixes=None,
     layout "contiguous": sequence b occupies pool rows [off_b, off_b + N_b) in
     order (identity slots for batch 1). layout "random": one seeded random
     permutation of a pool of ``pool_factor`` x total tokens; sequence b takes
-    the next N_b entries of it. mask "tree" draws parent(i) uniformly from
+    the next N_b entries of it. layout "sorted": the same random choice of
+    rows, sorted ascending before it is handed out. mask "tree" draws parent(i) uniformly from
     {-1, .., i-1} unless ``parents`` is given. ``prefix_range=(lo, hi)``
     draws each sequence's prefix uniformly from [lo, hi] instead.
     """
@@ -117,6 +118,12 @@ def make_verify(name: str, *, batch: int, q_len: int, heads: int, prefixes=None,
         pool_rows = pool_factor * total
         ref_rows = _normal_bf16(rng, (total, DK))
         perm = rng.permutation(pool_rows)[:total]
+    elif layout == "sorted":
+        # a sorted free list over a fragmented pool: the same random choice of
+        # free rows, handed out in ascending order (runs with gaps)
+        pool_rows = pool_factor * total
+        ref_rows = _normal_bf16(rng, (total, DK))
+        perm = np.sort(rng.permutation(pool_rows)[:total])
     else:
         raise ValueError(layout)
     pool_bits = np.full((pool_rows, DK), BF16_NAN, dtype=np.uint16)
@@ -195,6 +202,9 @@ def workload(name: str, seed: Optional[int] = None) -> VerifyInputs:
     c2          batch 1, q_len 9, H 64, prefix 4096, contiguous, causal (seed 2)
     c3_16k      batch 1, q_len 9, H 8, prefix 16384, random slots in a 2x pool, causal (seed 3)
     c3_64k      same at prefix 65536 (seed 4)
+    c3_<P>_contig, c3_<P>_sorted (P in 16k, 64k)
+                the same call with contiguous slots, or with the random rows
+                handed out in ascending order (seeds 3, 4)
     c4          8 sequences, prefixes U{1024..32768}, H 64, 9-node random tree,
                 random slots in a 2x pool (seed 5)
     c5          batch 32, q_len 1, H 64, prefix 65536, fp8 latent, top-k 2048 (seed 6)
@@ -208,6 +218,11 @@ def workload(name: str, seed: Optional[int] = None) -> VerifyInputs:
         return make_verify(name, batch=1, q_len=9, heads=8, prefixes=16384, seed=seed or 3, layout="random")
     if name == "c3_64k":
         return make_verify(name, batch=1, q_len=9, heads=8, prefixes=65536, seed=seed or 4, layout="random")
+    for p, sd in (("16k", 3), ("64k", 4)):
+        for lay, tag in (("contiguous", "contig"), ("sorted", "sorted")):
+            if name == f"c3_{p}_{tag}":
+                return make_verify(name, batch=1, q_len=9, heads=8, prefixes=16384 if p == "16k" else 65536,
+                                   seed=seed or sd, layout=lay)
     if name == "c4":
         return make_verify(name, batch=8, q_len=9, heads=64, prefix_range=(1024, 32768), seed=seed or 5,
                            layout="random", mask="tree")

@@ -38,6 +38,12 @@ Readings of points the pages leave open:
 9. Split s of S covers [s*c, min(N, (s+1)*c)) with c = ceil(N / S); an empty
    split contributes (lse=-inf, O=0).
 10. An empty visible set gives out = 0 and lse = -inf.
+11. Draft-KV append (the step before a verify call): the q_len new rows of
+    sequence b land at the pool rows of positions N_b - q_len .. N_b - 1 of
+    its slot table, consistent with reading 4 ("How One Environment
+    Variable Unlocked 3x Throughput", section *The Central Dilemma*: each
+    request's KV sits in allocator-assigned slots). Every other pool row is
+    untouched.
 """
 
 from __future__ import annotations
@@ -347,3 +353,18 @@ def brute_force_sparse(q_bits, lat_bits, rope_bits, scale, slot_table, topk_idx,
                 for c in range(DV):
                     out[b, i, h, c] = math.fsum(w * kk[c] for w, kk in zip(ws, keys)) / tot
     return out, lse
+
+
+def append_kv(pool_bits: np.ndarray, new_bits: np.ndarray, slot_table: np.ndarray, seq_lens: np.ndarray):
+    """Pool after the draft-KV append of reading 11 (a new array; the input is not modified).
+
+    new_bits: bf16 bits [batch, q_len, 576]; the row of draft i of sequence b
+    is stored at pool row slot_table[b, seq_lens[b] - q_len + i].
+    """
+    out = np.array(pool_bits, copy=True)
+    bsz, q_len = new_bits.shape[:2]
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        for i in range(q_len):
+            out[int(slot_table[b, n - q_len + i])] = new_bits[b, i]
+    return out

@@ -359,3 +359,36 @@ def test_generator_shapes_and_poison():
     unused = np.setdiff1d(np.arange(w4.pool_rows), used)
     assert (w4.pool_bits[unused] == 0x7FC0).all()
     assert all(-1 <= w4.parents[b, i] < i for b in range(3) for i in range(9))
+
+
+# ---------------------------------------------------------------- P8 draft-KV append
+def test_append_worked_example():
+    # Pool of 6 rows, each filled with its own index; two sequences of two
+    # drafts each. Sequence 0: slots [5, 1, 3, 0], length 4 -> positions 2, 3
+    # -> rows 3 and 0. Sequence 1: slots [2, 4, 9, 9], length 2 -> positions
+    # 0, 1 -> rows 2 and 4. New rows carry 100 + 10 b + i.
+    pool = np.repeat(np.arange(6, dtype=np.uint16)[:, None], O.DK, axis=1)
+    new = np.array([[100, 101], [110, 111]], dtype=np.uint16)[:, :, None].repeat(O.DK, axis=2)
+    slots = np.array([[5, 1, 3, 0], [2, 4, 9, 9]], dtype=np.int32)
+    lens = np.array([4, 2], dtype=np.int32)
+    got = O.append_kv(pool, new, slots, lens)
+    expected_rows = [101, 1, 110, 100, 111, 5]
+    assert [int(got[r, 0]) for r in range(6)] == expected_rows
+    assert (got == got[:, :1]).all()                       # whole rows move
+    assert [int(pool[r, 0]) for r in range(6)] == list(range(6))  # input untouched
+
+
+def test_append_restores_wiped_draft_rows():
+    # Round trip on a generated pool: wipe the rows the drafts occupy, append
+    # them again, get the generator's pool back bit for bit.
+    w = tiny(mask="causal", seed=41, batch=3, q_len=4)
+    pool = w.pool_bits.copy()
+    new = np.zeros((w.batch, w.q_len, O.DK), dtype=np.uint16)
+    for b in range(w.batch):
+        n = int(w.seq_lens[b])
+        for i in range(w.q_len):
+            row = int(w.slot_table[b, n - w.q_len + i])
+            new[b, i] = pool[row]
+            pool[row] = 0x7FC0
+    back = O.append_kv(pool, new, w.slot_table, w.seq_lens)
+    np.testing.assert_array_equal(back, w.pool_bits)
