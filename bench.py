@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--nsplit", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough for > 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="verify", choices=["verify", "append"],
-                    help="append: time the draft-KV append (mla_append_kv) for the workload's shape instead")
+    ap.add_argument("--op", default="verify", choices=["verify", "append", "topk"],
+                    help="append: time the draft-KV append (mla_append_kv) for the workload's shape instead; "
+                         "topk: time the top-k selection (mla_topk_select) feeding a sparse workload")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -195,6 +196,9 @@ def main():
     if args.op == "append":
         bench_append(args, w)
         return
+    if args.op == "topk":
+        bench_topk(args, w)
+        return
     if w.kind == "sparse":
         cnt = RL.sparse_counts(w.batch, w.q_len, w.heads, w.meta["topk"])
         read_bytes = w.batch * w.q_len * w.meta["topk"] * 652
@@ -316,6 +320,49 @@ def bench_append(args, w):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded bf16 bit patterns",
         "config": {"workload": describe(w), "rows": rows},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(ach / 8000.0, 5), "traffic": None},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def bench_topk(args, w):
+    """One JSON line for the top-k selection that would feed the sparse workload `w`: one fp32 score per
+    prefix position and query, seeded N(0,1), top-k of them."""
+    import numpy as np
+    import torch
+
+    from mla_speculative_decode_verify_amd import binding as B
+
+    assert w.kind == "sparse", "the top-k selection feeds a sparse workload"
+    n, k = int(w.meta["prefix"]), int(w.meta["topk"])
+    rng = np.random.default_rng(78)
+    scores = rng.standard_normal((w.batch, w.q_len, n)).astype(np.float32)
+    lens = np.full(w.batch, n, dtype=np.int32)
+    s_t, l_t = torch.from_numpy(scores).cuda(), torch.from_numpy(lens).cuda()
+    out = B.topk_select(s_t, l_t, k)  # validates once
+    L = B.lib()
+    cargs = (s_t.data_ptr(), w.batch, w.q_len, n, l_t.data_ptr(), k, out.data_ptr(),
+             int(torch.cuda.current_stream().cuda_stream))
+    call = lambda: L.mla_topk_select(*cargs)  # noqa: E731
+    us = time_calls([call], args.steps, args.warmup, rotate=False)
+    rows = w.batch * w.q_len
+    nbytes = rows * n * 4 + rows * k * 4 + w.batch * 4
+    log(f"[bench] topk {rows} rows of {n}: {us:.2f} us/call")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import mla_oracle as O
+
+        t0 = time.perf_counter()
+        O.topk_select(scores[:1, :1], lens[:1], k)
+        dt = (time.perf_counter() - t0) * 1e6
+        cpu = {"value": round(dt * rows, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+               "sample": f"one row of {n} scores, scaled by the {rows} rows of a call"}
+    ach = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "top-k selection µs/call", "value": round(us, 3), "unit": "us/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic: seeded N(0,1) fp32 scores",
+        "config": {"workload": f"top-{k} of {n} scores, {rows} rows (feeds {w.name})", "rows": rows},
         "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(ach / 8000.0, 5), "traffic": None},
         "cpu_baseline": cpu}), flush=True)

@@ -232,6 +232,25 @@ int mla_build_tree_mask_host(const int32_t* parents, int batch, int q_len, uint6
 int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* new_rows, int batch, int q_len,
                   const int32_t* slot_table, const int32_t* seq_lens, hipStream_t stream);
 
+/* Top-k selection feeding the sparse decode: for each (sequence b, query i)
+ * row of scores, the topk positions p < seq_lens[b] with the largest
+ * scores[b, i, p], written to topk_idx[b, i, 0..topk) in ascending position
+ * order. Ties go to the lower position, so the result is unique. Scores
+ * compare as floats with -0.0 below +0.0 and NaN below every number.
+ * ("The Occupancy Probe: A Methodical Approach to GPU Kernel
+ * Optimization", sections "The Thinking Process: Risk Assessment and
+ * Safety" and "Assumptions and Potential Pitfalls": a sparse indexer kernel
+ * picks the top-k positions each query of the sparse decode attends to; the
+ * pages give no scoring formula, so the scores are an input here.)
+ *   scores:   device fp32 [batch, q_len, score_stride] (16-byte aligned).
+ *   seq_lens: device int32 [batch]: positions [0, seq_lens[b]) are eligible.
+ *   topk_idx: device int32 [batch, q_len, topk], written.
+ * A row with seq_lens[b] < topk (or outside [0, score_stride]) sets
+ * MLA_DEVERR_SEQ_LEN and gets its positions 0 .. n-1 followed by -1.
+ * Enqueued on `stream`; allocates nothing but the device error flag. */
+int mla_topk_select(const float* scores, int batch, int q_len, int score_stride, const int32_t* seq_lens,
+                    int topk, int32_t* topk_idx, hipStream_t stream);
+
 /* Read (and optionally clear) the current device's sticky error flags.
  * Synchronises the device. Returns the MLA_DEVERR_* bits, or a negative
  * status code. */

@@ -100,6 +100,9 @@ def lib() -> ctypes.CDLL:
     L.mla_append_kv.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_append_kv.restype = ctypes.c_int
+    L.mla_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_topk_select.restype = ctypes.c_int
     L.mla_get_device_error.argtypes = [ctypes.c_int]
     L.mla_get_device_error.restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
@@ -291,6 +294,23 @@ def append_kv(kv, new_rows, slot_table, seq_lens, stream=None):
     _check(lib().mla_append_kv(kv.data_ptr(), int(kv.shape[0]), int(slot_table.shape[1]), new_rows.data_ptr(), bsz,
                                q_len, slot_table.data_ptr(), seq_lens.data_ptr(), _stream_handle(stream)),
            "mla_append_kv")
+
+
+def topk_select(scores, seq_lens, topk: int, out=None, stream=None):
+    """Top-k positions (int32 [B, Q, topk], ascending) of fp32 scores [B, Q, S] below seq_lens[b]."""
+    import torch
+
+    _req(scores, torch.float32, "scores")
+    if scores.dim() != 3:
+        raise ValueError("scores must be [B, Q, S]")
+    bsz, q_len, stride = (int(x) for x in scores.shape)
+    _req(seq_lens, torch.int32, "seq_lens", (bsz,))
+    if out is None:
+        out = torch.empty((bsz, q_len, topk), dtype=torch.int32, device=scores.device)
+    _req(out, torch.int32, "out", (bsz, q_len, topk))
+    _check(lib().mla_topk_select(scores.data_ptr(), bsz, q_len, stride, seq_lens.data_ptr(), int(topk),
+                                 out.data_ptr(), _stream_handle(stream)), "mla_topk_select")
+    return out
 
 
 def build_tree_mask_host(parents: np.ndarray) -> np.ndarray:

@@ -404,6 +404,22 @@ int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* 
              : MLA_ERR_LAUNCH;
 }
 
+int mla_topk_select(const float* scores, int batch, int q_len, int score_stride, const int32_t* seq_lens,
+                    int topk, int32_t* topk_idx, hipStream_t stream) {
+  if (!scores || !seq_lens || !topk_idx) return MLA_ERR_INVALID_ARG;
+  if (batch < 1 || q_len < 1 || score_stride < 1 || topk < 1) return MLA_ERR_INVALID_ARG;
+  if ((long)batch * q_len > 0x7fffffffL) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(scores, 16) || !aligned(seq_lens, 4) || !aligned(topk_idx, 4)) return MLA_ERR_ALIGN;
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  unsigned* err = nullptr;
+  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  return mla::launch_topk(scores, batch, q_len, score_stride, seq_lens, topk, topk_idx, err, stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_LAUNCH;
+}
+
 int mla_get_device_error(int clear) {
   int dev = 0;
   int st = current_device(&dev);

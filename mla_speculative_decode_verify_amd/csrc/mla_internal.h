@@ -54,6 +54,10 @@ hipError_t launch_combine(const Args& a, hipStream_t stream);
 hipError_t launch_append(void* latent, int64_t pool_rows, int slot_stride, const void* new_rows, int batch,
                          int q_len, const int32_t* slots, const int32_t* seq_lens, unsigned* err,
                          hipStream_t stream);
+// Top-k selection: per (sequence, query) row of scores, the topk best
+// positions below seq_lens[b], in ascending order.
+hipError_t launch_topk(const float* scores, int batch, int q_len, int score_stride, const int32_t* seq_lens,
+                       int topk, int32_t* out, unsigned* err, hipStream_t stream);
 // Ancestor-or-self masks from parent arrays.
 hipError_t launch_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* anc, unsigned* err,
                             hipStream_t stream);

@@ -44,6 +44,13 @@ Readings of points the pages leave open:
     Variable Unlocked 3x Throughput", section *The Central Dilemma*: each
     request's KV sits in allocator-assigned slots). Every other pool row is
     untouched.
+12. Top-k selection feeding the sparse decode (a sparse indexer kernel, "The
+    Occupancy Probe", sections *The Thinking Process* and *Assumptions and
+    Potential Pitfalls*; the pages give no scoring formula): the topk
+    eligible positions with the largest scores, ties to the lower position,
+    listed in ascending position order. Scores compare as real numbers with
+    -0.0 below +0.0 and NaN below every number. A row with fewer eligible
+    positions than topk lists them all, then -1.
 """
 
 from __future__ import annotations
@@ -367,4 +374,23 @@ def append_kv(pool_bits: np.ndarray, new_bits: np.ndarray, slot_table: np.ndarra
         n = int(seq_lens[b])
         for i in range(q_len):
             out[int(slot_table[b, n - q_len + i])] = new_bits[b, i]
+    return out
+
+
+def topk_select(scores: np.ndarray, seq_lens: np.ndarray, topk: int) -> np.ndarray:
+    """Reading 12, straight from its statement: rank every eligible position by
+    (score, then lower position first) and keep the best topk, listed ascending."""
+    bsz, q_len, _ = scores.shape
+    out = np.full((bsz, q_len, topk), -1, dtype=np.int32)
+    for b in range(bsz):
+        n = max(0, min(int(seq_lens[b]), scores.shape[2]))
+        for i in range(q_len):
+            def rank(p):
+                x = float(scores[b, i, p])
+                if math.isnan(x):
+                    return (0, 0.0, 0, -p)
+                return (1, x, 0 if (x == 0.0 and math.copysign(1.0, x) < 0) else 1, -p)
+            best = sorted(range(n), key=rank, reverse=True)[:topk]
+            best.sort()
+            out[b, i, :len(best)] = best
     return out

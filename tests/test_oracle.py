@@ -392,3 +392,45 @@ def test_append_restores_wiped_draft_rows():
             pool[row] = 0x7FC0
     back = O.append_kv(pool, new, w.slot_table, w.seq_lens)
     np.testing.assert_array_equal(back, w.pool_bits)
+
+
+# ---------------------------------------------------------------- P9 top-k selection
+def test_topk_worked_example():
+    # Eight positions, seq_len 7 (position 7 is not eligible even though its
+    # score is the largest). Scores by position:
+    #   0: 1.0  1: 3.0  2: -0.0  3: 3.0  4: nan  5: 0.0  6: 2.0  7: 9.0
+    # Best three: 1 (3.0), 3 (3.0, tie after 1), 6 (2.0) -> [1, 3, 6].
+    # Best five adds 0 (1.0) and 5 (+0.0 above -0.0) -> [0, 1, 3, 5, 6].
+    # Best seven takes everything eligible, NaN last -> [0..6].
+    s = np.array([[[1.0, 3.0, -0.0, 3.0, np.nan, 0.0, 2.0, 9.0]]], dtype=np.float32)
+    lens = np.array([7], dtype=np.int32)
+    assert O.topk_select(s, lens, 3).tolist() == [[[1, 3, 6]]]
+    assert O.topk_select(s, lens, 5).tolist() == [[[0, 1, 3, 5, 6]]]
+    assert O.topk_select(s, lens, 6).tolist() == [[[0, 1, 2, 3, 5, 6]]]
+    assert O.topk_select(s, lens, 7).tolist() == [[[0, 1, 2, 3, 4, 5, 6]]]
+    # fewer eligible positions than topk: all of them, then -1
+    assert O.topk_select(s, np.array([2], dtype=np.int32), 4).tolist() == [[[0, 1, -1, -1]]]
+
+
+def test_topk_matches_a_stable_sort_on_distinct_scores():
+    # With distinct finite scores the selection is the argsort's top k.
+    rng = np.random.default_rng(60)
+    s = rng.permutation(5000).astype(np.float32).reshape(2, 1, 2500) - 1000.0
+    lens = np.array([2500, 1800], dtype=np.int32)
+    got = O.topk_select(s, lens, 100)
+    for b in range(2):
+        n = int(lens[b])
+        ref = np.sort(np.argsort(-s[b, 0, :n], kind="stable")[:100])
+        np.testing.assert_array_equal(got[b, 0], ref)
+
+
+def test_topk_ties_go_to_lower_positions():
+    # Four distinct values, many ties: the kept ties are the lowest positions.
+    rng = np.random.default_rng(61)
+    s = rng.integers(0, 4, size=(1, 1, 400)).astype(np.float32)
+    lens = np.array([400], dtype=np.int32)
+    k = int((s == 3).sum()) + 10            # all of value 3, then the first ten 2s
+    got = O.topk_select(s, lens, k)[0, 0]
+    threes = np.nonzero(s[0, 0] == 3)[0]
+    twos = np.nonzero(s[0, 0] == 2)[0][:10]
+    np.testing.assert_array_equal(got, np.sort(np.concatenate([threes, twos])))
