@@ -242,7 +242,10 @@ int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* 
  * Safety" and "Assumptions and Potential Pitfalls": a sparse indexer kernel
  * picks the top-k positions each query of the sparse decode attends to; the
  * pages give no scoring formula, so the scores are an input here.)
- *   scores:   device fp32 [batch, q_len, score_stride] (16-byte aligned).
+ *   scores:   device fp32 [batch, q_len, score_stride], 16-byte aligned,
+ *             score_stride a multiple of 4 (else MLA_ERR_ALIGN) and at
+ *             most 67584 (else MLA_ERR_UNSUPPORTED: a row is held in
+ *             one workgroup's registers).
  *   seq_lens: device int32 [batch]: positions [0, seq_lens[b]) are eligible.
  *   topk_idx: device int32 [batch, q_len, topk], written.
  * A row with seq_lens[b] < topk (or outside [0, score_stride]) sets

@@ -408,8 +408,9 @@ int mla_topk_select(const float* scores, int batch, int q_len, int score_stride,
                     int topk, int32_t* topk_idx, hipStream_t stream) {
   if (!scores || !seq_lens || !topk_idx) return MLA_ERR_INVALID_ARG;
   if (batch < 1 || q_len < 1 || score_stride < 1 || topk < 1) return MLA_ERR_INVALID_ARG;
-  if ((long)batch * q_len > 0x7fffffffL) return MLA_ERR_UNSUPPORTED;
-  if (!aligned(scores, 16) || !aligned(seq_lens, 4) || !aligned(topk_idx, 4)) return MLA_ERR_ALIGN;
+  if ((long)batch * q_len > 0x7fffffffL || score_stride > 67584) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(scores, 16) || score_stride % 4 != 0 || !aligned(seq_lens, 4) || !aligned(topk_idx, 4))
+    return MLA_ERR_ALIGN;
   int dev = 0;
   int st = current_device(&dev);
   if (st != MLA_OK) return st;

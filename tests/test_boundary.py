@@ -164,3 +164,27 @@ def test_host_tree_mask_rejects_bad_parents(L):
         assert e.value.status == B.MLA_ERR_INVALID_ARG
     with pytest.raises(B.MlaError):
         B.build_tree_mask_host(np.zeros((1, 65), dtype=np.int32) - 1)
+
+
+@pytest.mark.parametrize("args,code", [
+    # (scores, batch, q_len, score_stride, seq_lens, topk, out)
+    ((0, 1, 1, 64, FAKE, 8, FAKE), B.MLA_ERR_INVALID_ARG),             # null scores
+    ((FAKE, 0, 1, 64, FAKE, 8, FAKE), B.MLA_ERR_INVALID_ARG),          # no rows
+    ((FAKE, 1, 1, 64, FAKE, 0, FAKE), B.MLA_ERR_INVALID_ARG),          # topk 0
+    ((FAKE, 1, 1, 66, FAKE, 8, FAKE), B.MLA_ERR_ALIGN),                # stride not a multiple of 4
+    ((FAKE + 4, 1, 1, 64, FAKE, 8, FAKE), B.MLA_ERR_ALIGN),            # scores not 16-byte aligned
+    ((FAKE, 1, 1, 67588, FAKE, 8, FAKE), B.MLA_ERR_UNSUPPORTED),       # row longer than one workgroup holds
+])
+def test_topk_select_bad_arguments_rejected_before_launch(L, args, code):
+    assert L.mla_topk_select(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    # (latent, pool_rows, slot_stride, new_rows, batch, q_len, slot_table, seq_lens)
+    ((0, 10, 16, FAKE, 1, 4, FAKE, FAKE), B.MLA_ERR_INVALID_ARG),      # null pool
+    ((FAKE, 10, 3, FAKE, 1, 4, FAKE, FAKE), B.MLA_ERR_INVALID_ARG),    # slot_stride < q_len
+    ((FAKE, 10, 128, FAKE, 1, 65, FAKE, FAKE), B.MLA_ERR_UNSUPPORTED),  # q_len above 64
+    ((FAKE + 8, 10, 16, FAKE, 1, 4, FAKE, FAKE), B.MLA_ERR_ALIGN),      # pool not 16-byte aligned
+])
+def test_append_kv_bad_arguments_rejected_before_launch(L, args, code):
+    assert L.mla_append_kv(*args, None) == code
