@@ -44,9 +44,10 @@ def parse():
     ap.add_argument("--nsplit", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough for > 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="verify", choices=["verify", "append", "topk"],
+    ap.add_argument("--op", default="verify", choices=["verify", "append", "topk", "absorb"],
                     help="append: time the draft-KV append (mla_append_kv) for the workload's shape instead; "
-                         "topk: time the top-k selection (mla_topk_select) feeding a sparse workload")
+                         "topk: time the top-k selection (mla_topk_select) feeding a sparse workload; "
+                         "absorb: time the weight absorptions (mla_absorb_q + mla_project_o) for its rows")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -198,6 +199,9 @@ def main():
         return
     if args.op == "topk":
         bench_topk(args, w)
+        return
+    if args.op == "absorb":
+        bench_absorb(args, w)
         return
     if w.kind == "sparse":
         cnt = RL.sparse_counts(w.batch, w.q_len, w.heads, w.meta["topk"])
@@ -366,6 +370,47 @@ def bench_topk(args, w):
         "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(ach / 8000.0, 5), "traffic": None},
         "cpu_baseline": cpu}), flush=True)
+
+
+def bench_absorb(args, w):
+    """One JSON line for the query absorption plus the value projection of the workload's rows
+    (seeded N(0,1) activations, N(0,1)/sqrt(fan-in) weights, per-head widths 128)."""
+    import numpy as np
+    import torch
+
+    from mla_speculative_decode_verify_amd import binding as B
+    from mla_speculative_decode_verify_amd import inputs as I
+
+    T, H = w.batch * w.q_len, w.heads
+    rng = np.random.default_rng(79)
+    bf = lambda a: torch.from_numpy(I.f32_to_bf16_bits(a.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    qn, qr = bf(rng.standard_normal((T, H, 128))), bf(rng.standard_normal((T, H, 64)))
+    w_uk = bf(rng.standard_normal((H, 512, 128)) / 128 ** 0.5)
+    w_uv = bf(rng.standard_normal((H, 128, 512)) / 512 ** 0.5)
+    o_lat = torch.from_numpy(rng.standard_normal((T, H, 512)).astype(np.float32)).cuda()
+    q_out = B.absorb_q(qn, qr, w_uk)
+    o_out = B.project_o(o_lat, w_uv)
+    L = B.lib()
+    st = int(torch.cuda.current_stream().cuda_stream)
+    a1 = (qn.data_ptr(), qr.data_ptr(), w_uk.data_ptr(), T, H, q_out.data_ptr(), st)
+    a2 = (o_lat.data_ptr(), w_uv.data_ptr(), T, H, o_out.data_ptr(), st)
+    us_q = time_calls([lambda: L.mla_absorb_q(*a1)], args.steps, args.warmup, rotate=False)
+    us_o = time_calls([lambda: L.mla_project_o(*a2)], args.steps, args.warmup, rotate=False)
+    us = us_q + us_o
+    nbytes = 2 * H * 512 * 128 * 2 + T * H * (128 * 2 + 64 * 2 + 576 * 2 + 512 * 4 + 128 * 4)
+    flops = 2 * 2 * T * H * 512 * 128
+    log(f"[bench] absorb {T} rows x {H} heads: q {us_q:.2f} us, o {us_o:.2f} us")
+    ach = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "weight absorption µs/call (query + value projection)", "value": round(us, 3), "unit": "us/call",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations, N(0,1)/sqrt(fan-in) weights",
+        "config": {"workload": f"{T} rows x {H} heads (rows of {w.name}), per-head widths 128",
+                   "kernels_us": {"absorb_q": round(us_q, 3), "project_o": round(us_o, 3)}, "flops": flops},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(ach / 8000.0, 5), "traffic": None},
+        "cpu_baseline": None}), flush=True)
 
 
 KERNEL_SOURCES = {

@@ -254,6 +254,33 @@ int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* 
 int mla_topk_select(const float* scores, int batch, int q_len, int score_stride, const int32_t* seq_lens,
                     int topk, int32_t* topk_idx, hipStream_t stream);
 
+/* Weight absorption around the attention, as bf16 MFMA GEMMs with fp32
+ * accumulation. ("How a CUDA Kernel Designer Discovered That GPU Utilization
+ * Trumps Memory Bandwidth", section "The Warp-Per-Key Dot Product": scores
+ * are 576-element dot products; "The Occupancy Probe", section "The Scene":
+ * the latent accumulator is 512 wide per head.) The pages fix only the
+ * 576 / 512 widths;
+ * the per-head widths here, 128 for q_nope and 128 for the value, are the
+ * common MLA configuration (an assumption). tokens = rows of the call
+ * (batch * q_len); every pointer is device memory, 16-byte aligned.
+ *
+ * mla_absorb_q: q_out[t, h, 0:512] = q_nope[t, h, :] . W_UK[h] (rounded to
+ *   bf16) and q_out[t, h, 512:576] = q_rope[t, h, :], i.e. the absorbed
+ *   query mla_verify_attn takes.
+ *     q_nope bf16 [tokens, heads, 128]; q_rope bf16 [tokens, heads, 64];
+ *     w_uk bf16 [heads, 512, 128] (W_UK[h] transposed: row c holds the 128
+ *     weights of latent column c); q_out bf16 [tokens, heads, 576].
+ * mla_project_o: o_out[t, h, :] = o_latent[t, h, :] . W_UV[h], with o_latent
+ *   rounded to bf16 on the way in.
+ *     o_latent fp32 [tokens, heads, 512] (mla_verify_attn's out);
+ *     w_uv bf16 [heads, 128, 512] (W_UV[h] transposed: row c holds the 512
+ *     weights of value column c); o_out fp32 [tokens, heads, 128].
+ * Enqueued on `stream`; nothing is allocated. */
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int tokens, int heads, void* q_out,
+                 hipStream_t stream);
+int mla_project_o(const float* o_latent, const void* w_uv, int tokens, int heads, float* o_out,
+                  hipStream_t stream);
+
 /* Read (and optionally clear) the current device's sticky error flags.
  * Synchronises the device. Returns the MLA_DEVERR_* bits, or a negative
  * status code. */

@@ -103,6 +103,11 @@ def lib() -> ctypes.CDLL:
     L.mla_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_topk_select.restype = ctypes.c_int
+    L.mla_absorb_q.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_absorb_q.restype = ctypes.c_int
+    L.mla_project_o.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    L.mla_project_o.restype = ctypes.c_int
     L.mla_get_device_error.argtypes = [ctypes.c_int]
     L.mla_get_device_error.restype = ctypes.c_int
     L.mla_status_string.argtypes = [ctypes.c_int]
@@ -310,6 +315,37 @@ def topk_select(scores, seq_lens, topk: int, out=None, stream=None):
     _req(out, torch.int32, "out", (bsz, q_len, topk))
     _check(lib().mla_topk_select(scores.data_ptr(), bsz, q_len, stride, seq_lens.data_ptr(), int(topk),
                                  out.data_ptr(), _stream_handle(stream)), "mla_topk_select")
+    return out
+
+
+def absorb_q(q_nope, q_rope, w_uk, out=None, stream=None):
+    """Absorbed query bf16 [T, H, 576] = [q_nope . W_UK[h] | q_rope]; w_uk is bf16 [H, 512, 128] (transposed)."""
+    import torch
+
+    T, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _req(q_nope, torch.bfloat16, "q_nope", (T, H, 128))
+    _req(q_rope, torch.bfloat16, "q_rope", (T, H, 64))
+    _req(w_uk, torch.bfloat16, "w_uk", (H, 512, 128))
+    if out is None:
+        out = torch.empty((T, H, 576), dtype=torch.bfloat16, device=q_nope.device)
+    _req(out, torch.bfloat16, "out", (T, H, 576))
+    _check(lib().mla_absorb_q(q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(), T, H, out.data_ptr(),
+                              _stream_handle(stream)), "mla_absorb_q")
+    return out
+
+
+def project_o(o_latent, w_uv, out=None, stream=None):
+    """Per-head output fp32 [T, H, 128] = o_latent . W_UV[h]; w_uv is bf16 [H, 128, 512] (transposed)."""
+    import torch
+
+    T, H = int(o_latent.shape[0]), int(o_latent.shape[1])
+    _req(o_latent, torch.float32, "o_latent", (T, H, 512))
+    _req(w_uv, torch.bfloat16, "w_uv", (H, 128, 512))
+    if out is None:
+        out = torch.empty((T, H, 128), dtype=torch.float32, device=o_latent.device)
+    _req(out, torch.float32, "out", (T, H, 128))
+    _check(lib().mla_project_o(o_latent.data_ptr(), w_uv.data_ptr(), T, H, out.data_ptr(), _stream_handle(stream)),
+           "mla_project_o")
     return out
 
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_verify.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "split_bf16.hip", "split_fp8.hip", "combine.hip", "append.hip", "topk.hip"]
+SOURCES = ["api.cpp", "split_bf16.hip", "split_fp8.hip", "combine.hip", "append.hip", "topk.hip", "absorb.hip"]
 # Per-source extra compiler flags.
 EXTRA_FLAGS = {}
 

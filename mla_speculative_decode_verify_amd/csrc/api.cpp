@@ -421,6 +421,24 @@ int mla_topk_select(const float* scores, int batch, int q_len, int score_stride,
              : MLA_ERR_LAUNCH;
 }
 
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int tokens, int heads, void* q_out,
+                 hipStream_t stream) {
+  if (!q_nope || !q_rope || !w_uk || !q_out || tokens < 1 || heads < 1) return MLA_ERR_INVALID_ARG;
+  if (heads > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16) || !aligned(q_out, 16)) return MLA_ERR_ALIGN;
+  return mla::launch_absorb_q(q_nope, q_rope, w_uk, tokens, heads, q_out, stream) == hipSuccess ? MLA_OK
+                                                                                                : MLA_ERR_LAUNCH;
+}
+
+int mla_project_o(const float* o_latent, const void* w_uv, int tokens, int heads, float* o_out,
+                  hipStream_t stream) {
+  if (!o_latent || !w_uv || !o_out || tokens < 1 || heads < 1) return MLA_ERR_INVALID_ARG;
+  if (heads > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(o_latent, 16) || !aligned(w_uv, 16) || !aligned(o_out, 16)) return MLA_ERR_ALIGN;
+  return mla::launch_project_o(o_latent, w_uv, tokens, heads, o_out, stream) == hipSuccess ? MLA_OK
+                                                                                          : MLA_ERR_LAUNCH;
+}
+
 int mla_get_device_error(int clear) {
   int dev = 0;
   int st = current_device(&dev);

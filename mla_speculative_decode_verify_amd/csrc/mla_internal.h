@@ -58,6 +58,11 @@ hipError_t launch_append(void* latent, int64_t pool_rows, int slot_stride, const
 // positions below seq_lens[b], in ascending order.
 hipError_t launch_topk(const float* scores, int batch, int q_len, int score_stride, const int32_t* seq_lens,
                        int topk, int32_t* out, unsigned* err, hipStream_t stream);
+// Weight absorption around the attention (per-head widths 128 / 128).
+hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int tokens, int heads,
+                           void* q_out, hipStream_t stream);
+hipError_t launch_project_o(const float* o_latent, const void* w_uv, int tokens, int heads, float* o_out,
+                            hipStream_t stream);
 // Ancestor-or-self masks from parent arrays.
 hipError_t launch_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* anc, unsigned* err,
                             hipStream_t stream);

@@ -51,6 +51,11 @@ Readings of points the pages leave open:
     listed in ascending position order. Scores compare as real numbers with
     -0.0 below +0.0 and NaN below every number. A row with fewer eligible
     positions than topk lists them all, then -1.
+13. Weight absorption around the attention (the 576 = 512 + 64 query and
+    512-wide latent output of readings 1-3): q = [q_nope . W_UK[h] | q_rope]
+    and o = o_latent . W_UV[h]. The pages fix only the 576 / 512 widths; the
+    per-head widths 128 (q_nope) and 128 (value) are an assumption. Weights
+    are given transposed, W_UK^T [H, 512, 128] and W_UV^T [H, 128, 512].
 """
 
 from __future__ import annotations
@@ -393,4 +398,35 @@ def topk_select(scores: np.ndarray, seq_lens: np.ndarray, topk: int) -> np.ndarr
             best = sorted(range(n), key=rank, reverse=True)[:topk]
             best.sort()
             out[b, i, :len(best)] = best
+    return out
+
+
+def absorb_q(q_nope_bits, q_rope_bits, w_uk_t_bits):
+    """Reading 13, before the attention: fp64 [T, H, 576] = [q_nope . W_UK[h] | q_rope].
+
+    q_nope bf16 bits [T, H, 128]; q_rope bf16 bits [T, H, 64]; w_uk_t bf16 bits
+    [H, 512, 128] (W_UK[h] transposed: element [h, c, k] multiplies q_nope[.., k]
+    into latent column c).
+    """
+    qn = bf16_bits_to_f64(q_nope_bits)
+    w = bf16_bits_to_f64(w_uk_t_bits)
+    T, H, _ = qn.shape
+    out = np.zeros((T, H, DK))
+    for h in range(H):
+        out[:, h, :DV] = qn[:, h, :] @ w[h].T
+    out[:, :, DV:] = bf16_bits_to_f64(q_rope_bits)
+    return out
+
+
+def project_o(o_latent, w_uv_t_bits):
+    """Reading 13, after the attention: fp64 [T, H, 128] = o_latent . W_UV[h].
+
+    o_latent fp64 [T, H, 512]; w_uv_t bf16 bits [H, 128, 512] (element [h, c, k]
+    multiplies o_latent[.., k] into value column c).
+    """
+    w = bf16_bits_to_f64(w_uv_t_bits)
+    T, H, _ = o_latent.shape
+    out = np.zeros((T, H, w.shape[1]))
+    for h in range(H):
+        out[:, h, :] = o_latent[:, h, :] @ w[h].T
     return out

@@ -66,7 +66,7 @@ def oracle(w: VerifyInputs, heads=None):
 
 
 def compare(out, lse, ref_out, ref_lse, what=""):
-    """Assert the benchmark spec's tolerances; returns the metrics."""
+    """Assert the parity tolerances (output max-abs 1e-2 and relative L2 5e-3, LSE max-abs 1e-3); returns the metrics."""
     o = out.detach().float().cpu().numpy().astype(np.float64)
     l = lse.detach().float().cpu().numpy().astype(np.float64)
     assert np.isfinite(o).all(), f"{what}: non-finite output"

@@ -434,3 +434,42 @@ def test_topk_ties_go_to_lower_positions():
     threes = np.nonzero(s[0, 0] == 3)[0]
     twos = np.nonzero(s[0, 0] == 2)[0][:10]
     np.testing.assert_array_equal(got, np.sort(np.concatenate([threes, twos])))
+
+
+# ---------------------------------------------------------------- P10 weight absorption
+def _bits(x):
+    return I.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_absorb_identity_and_one_hot_weights():
+    rng = np.random.default_rng(80)
+    T, H = 3, 2
+    qn = _bits(rng.standard_normal((T, H, 128)))
+    qr = _bits(rng.standard_normal((T, H, 64)))
+    # W_UK[h] = identity on the first 128 latent columns, zero elsewhere
+    w = np.zeros((H, 512, 128), dtype=np.float32)
+    w[:, np.arange(128), np.arange(128)] = 1.0
+    out = O.absorb_q(qn, qr, _bits(w))
+    np.testing.assert_array_equal(out[:, :, :128], O.bf16_bits_to_f64(qn))
+    assert (out[:, :, 128:512] == 0).all()
+    np.testing.assert_array_equal(out[:, :, 512:], O.bf16_bits_to_f64(qr))
+    # one-hot weight: latent column 300 of head 1 reads q_nope element 7, times 2
+    w = np.zeros((H, 512, 128), dtype=np.float32)
+    w[1, 300, 7] = 2.0
+    out = O.absorb_q(qn, qr, _bits(w))
+    np.testing.assert_array_equal(out[:, 1, 300], 2.0 * O.bf16_bits_to_f64(qn)[:, 1, 7])
+    assert np.count_nonzero(out[:, :, :512]) == np.count_nonzero(O.bf16_bits_to_f64(qn)[:, 1, 7])
+
+
+def test_project_o_worked_example():
+    # Two latent values per token reach value column 5 of head 0 with weights
+    # 0.5 and -3: o = 0.5 * o[.., 10] - 3 * o[.., 511].
+    H = 1
+    o_lat = np.zeros((2, H, 512))
+    o_lat[0, 0, 10], o_lat[0, 0, 511] = 4.0, 1.0     # 0.5*4 - 3*1 = -1
+    o_lat[1, 0, 10], o_lat[1, 0, 511] = -2.0, 0.25   # -1 - 0.75 = -1.75
+    w = np.zeros((H, 128, 512), dtype=np.float32)
+    w[0, 5, 10], w[0, 5, 511] = 0.5, -3.0
+    out = O.project_o(o_lat, _bits(w))
+    assert out[0, 0, 5] == -1.0 and out[1, 0, 5] == -1.75
+    assert np.count_nonzero(out) == 2
