@@ -64,6 +64,8 @@ def test_c4_tree_ragged_sampled_heads():
     (64, 2, [70], "causal"),          # maximum q_len
     (9, 16, [1000, 37], "none"),      # no mask, ragged
     (7, 20, [300], "tree"),           # 140 rows -> several row groups
+    (2, 128, [513, 64], "causal"),    # the largest head count: 256 rows in row groups of 80
+    (9, 8, [int(x) for x in np.random.default_rng(3).integers(0, 700, size=40)], "tree"),  # 40 ragged sequences
 ])
 def test_edge_shapes(q_len, heads, prefixes, mask):
     w = I.make_verify(f"edge_q{q_len}_h{heads}_{mask}", batch=len(prefixes), q_len=q_len, heads=heads,
