@@ -244,15 +244,19 @@ int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* 
  * pages give no scoring formula, so the scores are an input here.)
  *   scores:   device fp32 [batch, q_len, score_stride], 16-byte aligned,
  *             score_stride a multiple of 4 (else MLA_ERR_ALIGN) and at
- *             most 67584 (else MLA_ERR_UNSUPPORTED: a row is held in
- *             one workgroup's registers).
+ *             most 2^20, with batch * q_len at most 65535 (else
+ *             MLA_ERR_UNSUPPORTED).
  *   seq_lens: device int32 [batch]: positions [0, seq_lens[b]) are eligible.
  *   topk_idx: device int32 [batch, q_len, topk], written.
  * A row with seq_lens[b] < topk (or outside [0, score_stride]) sets
  * MLA_DEVERR_SEQ_LEN and gets its positions 0 .. n-1 followed by -1.
- * Enqueued on `stream`; allocates nothing but the device error flag. */
+ * Enqueued on `stream` (four kernels, each row cut into parts of 8192
+ * positions); uses the library's workspace for (device, stream) like
+ * mla_verify_attn, mla_topk_workspace_bytes(batch, q_len, score_stride)
+ * bytes (reserve it with mla_reserve_workspace before graph capture). */
 int mla_topk_select(const float* scores, int batch, int q_len, int score_stride, const int32_t* seq_lens,
                     int topk, int32_t* topk_idx, hipStream_t stream);
+size_t mla_topk_workspace_bytes(int batch, int q_len, int score_stride);
 
 /* Weight absorption around the attention, as bf16 MFMA GEMMs with fp32
  * accumulation. ("How a CUDA Kernel Designer Discovered That GPU Utilization

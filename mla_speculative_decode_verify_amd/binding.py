@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
     L.mla_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_topk_select.restype = ctypes.c_int
+    L.mla_topk_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.mla_topk_workspace_bytes.restype = ctypes.c_size_t
     L.mla_absorb_q.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_absorb_q.restype = ctypes.c_int
     L.mla_project_o.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -347,6 +349,10 @@ def project_o(o_latent, w_uv, out=None, stream=None):
     _check(lib().mla_project_o(o_latent.data_ptr(), w_uv.data_ptr(), T, H, out.data_ptr(), _stream_handle(stream)),
            "mla_project_o")
     return out
+
+
+def topk_workspace_bytes(batch: int, q_len: int, score_stride: int) -> int:
+    return int(lib().mla_topk_workspace_bytes(batch, q_len, score_stride))
 
 
 def build_tree_mask_host(parents: np.ndarray) -> np.ndarray:

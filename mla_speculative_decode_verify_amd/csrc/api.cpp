@@ -408,7 +408,7 @@ int mla_topk_select(const float* scores, int batch, int q_len, int score_stride,
                     int topk, int32_t* topk_idx, hipStream_t stream) {
   if (!scores || !seq_lens || !topk_idx) return MLA_ERR_INVALID_ARG;
   if (batch < 1 || q_len < 1 || score_stride < 1 || topk < 1) return MLA_ERR_INVALID_ARG;
-  if ((long)batch * q_len > 0x7fffffffL || score_stride > 67584) return MLA_ERR_UNSUPPORTED;
+  if ((long)batch * q_len > 65535 || score_stride > (1 << 20)) return MLA_ERR_UNSUPPORTED;
   if (!aligned(scores, 16) || score_stride % 4 != 0 || !aligned(seq_lens, 4) || !aligned(topk_idx, 4))
     return MLA_ERR_ALIGN;
   int dev = 0;
@@ -416,9 +416,17 @@ int mla_topk_select(const float* scores, int batch, int q_len, int score_stride,
   if (st != MLA_OK) return st;
   unsigned* err = nullptr;
   if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
-  return mla::launch_topk(scores, batch, q_len, score_stride, seq_lens, topk, topk_idx, err, stream) == hipSuccess
+  void* ws = nullptr;
+  if ((st = workspace(dev, stream, mla::topk_workspace_bytes(batch * q_len, score_stride), &ws)) != MLA_OK) return st;
+  return mla::launch_topk(scores, batch, q_len, score_stride, seq_lens, topk, topk_idx, err, ws, stream) ==
+                 hipSuccess
              ? MLA_OK
              : MLA_ERR_LAUNCH;
+}
+
+size_t mla_topk_workspace_bytes(int batch, int q_len, int score_stride) {
+  if (batch < 1 || q_len < 1 || score_stride < 1) return 0;
+  return mla::topk_workspace_bytes(batch * q_len, score_stride);
 }
 
 int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int tokens, int heads, void* q_out,

@@ -57,7 +57,8 @@ hipError_t launch_append(void* latent, int64_t pool_rows, int slot_stride, const
 // Top-k selection: per (sequence, query) row of scores, the topk best
 // positions below seq_lens[b], in ascending order.
 hipError_t launch_topk(const float* scores, int batch, int q_len, int score_stride, const int32_t* seq_lens,
-                       int topk, int32_t* out, unsigned* err, hipStream_t stream);
+                       int topk, int32_t* out, unsigned* err, void* workspace, hipStream_t stream);
+size_t topk_workspace_bytes(int rows, int score_stride);
 // Weight absorption around the attention (per-head widths 128 / 128).
 hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int tokens, int heads,
                            void* q_out, hipStream_t stream);

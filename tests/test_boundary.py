@@ -173,7 +173,8 @@ def test_host_tree_mask_rejects_bad_parents(L):
     ((FAKE, 1, 1, 64, FAKE, 0, FAKE), B.MLA_ERR_INVALID_ARG),          # topk 0
     ((FAKE, 1, 1, 66, FAKE, 8, FAKE), B.MLA_ERR_ALIGN),                # stride not a multiple of 4
     ((FAKE + 4, 1, 1, 64, FAKE, 8, FAKE), B.MLA_ERR_ALIGN),            # scores not 16-byte aligned
-    ((FAKE, 1, 1, 67588, FAKE, 8, FAKE), B.MLA_ERR_UNSUPPORTED),       # row longer than one workgroup holds
+    ((FAKE, 1, 1, (1 << 20) + 4, FAKE, 8, FAKE), B.MLA_ERR_UNSUPPORTED),  # rows longer than 2^20
+    ((FAKE, 300, 256, 64, FAKE, 8, FAKE), B.MLA_ERR_UNSUPPORTED),      # more than 65535 rows
 ])
 def test_topk_select_bad_arguments_rejected_before_launch(L, args, code):
     assert L.mla_topk_select(*args, None) == code
@@ -188,3 +189,9 @@ def test_topk_select_bad_arguments_rejected_before_launch(L, args, code):
 ])
 def test_append_kv_bad_arguments_rejected_before_launch(L, args, code):
     assert L.mla_append_kv(*args, None) == code
+
+
+def test_topk_workspace_bytes(L):
+    # per row: 8 parts of 8192 positions -> histograms, candidate pairs, row and part counters
+    assert B.topk_workspace_bytes(32, 1, 65536) == 32 * (8 * 2048 * 4 + 8 * 8192 * 8 + 16 + 8 * 12)
+    assert B.topk_workspace_bytes(0, 1, 64) == 0
