@@ -52,3 +52,27 @@ def test_graph_replay_matches_eager(name, nsplit):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
     assert B.device_error() == 0
+
+
+def test_graph_replay_topk_matches_eager():
+    # the top-k selection uses the workspace too: reserved first, then captured
+    import numpy as np
+
+    rng = np.random.default_rng(3)
+    scores = torch.from_numpy(rng.standard_normal((4, 2, 20000)).astype(np.float32)).cuda()
+    lens = torch.tensor([20000, 9000, 300, 19999], dtype=torch.int32).cuda()
+    ref = B.topk_select(scores, lens, 512)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    B.reserve_workspace(B.topk_workspace_bytes(4, 2, 20000), stream=s)
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.topk_select(scores, lens, 512, out=out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
