@@ -61,6 +61,7 @@ def test_graph_replay_topk_matches_eager():
     rng = np.random.default_rng(3)
     scores = torch.from_numpy(rng.standard_normal((4, 2, 20000)).astype(np.float32)).cuda()
     lens = torch.tensor([20000, 9000, 300, 19999], dtype=torch.int32).cuda()
+    B.device_error()
     ref = B.topk_select(scores, lens, 512)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
@@ -76,3 +77,5 @@ def test_graph_replay_topk_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
+    # the 300-position row is shorter than topk: flagged (and the flag cleared here)
+    assert B.device_error() == B.MLA_DEVERR_SEQ_LEN
