@@ -52,6 +52,13 @@ def test_c3_64k_random_slots():
     _check(I.workload("c3_64k"), [16, 64, 128, 0])
 
 
+def test_h64_prefix_64k_sampled_heads():
+    # the pages' largest sweep point: q_len 9, H=64, prefix 65536 (every head
+    # computed on the GPU; the oracle checks a sample of them)
+    w = I.workload("sweep_65536")
+    _check(w, [0, 16], heads=[0, 31, 63])
+
+
 def test_c4_tree_ragged_sampled_heads():
     w = I.workload("c4")
     _check(w, [0, 8], heads=[0, 17, 63])
