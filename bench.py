@@ -269,7 +269,8 @@ def main():
         "config": {"workload": describe(w), "batch": w.batch, "q_len": w.q_len, "heads": w.heads,
                    "prefix": (w.meta["prefix"] if w.kind == "sparse" else
                               w.meta["prefixes"][0] if len(set(w.meta["prefixes"])) == 1 else w.meta["prefixes"]),
-                   "nsplit": plan["nsplit"], "waves_per_group": plan["waves_per_group"],
+                   "nsplit": plan["nsplit"], "balanced_splits": bool(plan["balanced"]),
+                   "waves_per_group": plan["waves_per_group"],
                    "row_groups": plan["row_groups"], "grid": plan["grid"], "cold_copies": copies},
         "warm_us": round(warm, 3),
         "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3)},

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 1
+#define MLA_VERIFY_ABI_VERSION 2
 
 /* Status codes. */
 #define MLA_OK 0
@@ -136,6 +136,8 @@ typedef struct mla_plan_t {
   size_t workspace_bytes;/* partial storage needed (0 when nsplit == 1) */
   int kernel;            /* 0 = bf16 verify, 1 = fp8 top-k sparse */
   int row_blocks;        /* 16-row query blocks per workgroup */
+  int balanced;          /* 1: split counts follow the sequence lengths (see
+                            mla_verify_attn); nsplit is then their upper bound */
 } mla_plan_t;
 
 /*
@@ -148,8 +150,17 @@ typedef struct mla_plan_t {
  *               prefix length bounding the top-k positions.
  *   out:        fp32 [batch, q_len, heads, 512].
  *   lse:        fp32 [batch, q_len, heads] or NULL.
- *   nsplit:     KV splits per sequence; <= 0 picks one from the CU count
- *               (mla_choose_nsplit). Capped at MLA_MAX_NSPLIT.
+ *   nsplit:     KV splits per sequence; <= 0 lets the library choose
+ *               from the CU count: one count for every sequence
+ *               (mla_choose_nsplit) when batch == 1, an fp8 cache or
+ *               batch > 64; otherwise (bf16 cache, 2..64 sequences) counts
+ *               that follow each sequence's length, derived on the device
+ *               from seq_lens, so that every split holds about the same
+ *               number of 32-position tiles and the grid (one workgroup per
+ *               CU at most) is not held up by the longest sequence. A
+ *               sequence of t tiles then gets ceil(t / T) splits, at most
+ *               ceil(t / 4) and at least 1, for the smallest T that keeps
+ *               the total within the grid. Capped at MLA_MAX_NSPLIT.
  * When nsplit > 1 the call uses the library's workspace for (device,
  * stream): it grows on demand (synchronising `stream` first), or returns
  * MLA_ERR_WORKSPACE if the stream is capturing and the reserve is too small.

@@ -63,6 +63,9 @@ bool stream_capturing(hipStream_t s) {
 // error word at offset 0 and a zero cache row at kZeroRowOffset.
 constexpr size_t kDevBlockBytes = 4096;
 constexpr size_t kZeroRowOffset = 256;
+// Largest batch whose split counts may follow the sequence lengths: the
+// kernels derive them with one sequence per lane of a wavefront.
+constexpr int kBalanceMaxBatch = 64;
 
 int error_word(int dev, hipStream_t stream, unsigned** out) {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -222,8 +225,25 @@ int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsp
   const int seqlen_for_split = c->kernel == 1 ? std::min(maxlen, m->topk) : maxlen;
   int s = nsplit > 0 ? nsplit : choose_nsplit_impl(q->batch, q->q_len, q->heads, seqlen_for_split, kv->dtype, num_cus);
   if (s > MLA_MAX_NSPLIT) return MLA_ERR_INVALID_ARG;
+  c->a.balance_units = 0;
+  if (nsplit <= 0 && c->kernel == 0 && q->batch >= 2 && q->batch <= kBalanceMaxBatch) {
+    // Ragged batch, library-chosen splits: per-sequence split counts that
+    // follow the lengths (balanced_split in the kernels), `units` splits in
+    // all so the grid runs in one pass. s becomes the partials' stride: the
+    // most one sequence can take (all others get one), at least 4 tiles each.
+    const long units = num_cus / c->groups;
+    const long tiles = ((long)maxlen + 31) / 32;
+    const long smax = std::min<long>({(long)MLA_MAX_NSPLIT, units - q->batch + 1, std::max<long>(1, (tiles + 3) / 4)});
+    // (the kernels sum the tile counts in 32-bit integers)
+    const long stride_tiles = ((long)kv->slot_stride + 31) / 32;
+    if (units > q->batch && smax >= 2 && (long)q->batch * stride_tiles < (1L << 30)) {
+      // no more units than the splits the caps allow
+      c->a.balance_units = (int)std::min<long>(units, (long)q->batch * smax);
+      s = (int)smax;
+    }
+  }
   // workgroup units of the 1-D split grid, indexed with int on the device
-  const long units = key_sets * s * c->groups;
+  const long units = (c->a.balance_units > 0 ? c->a.balance_units : key_sets * s) * c->groups;
   if (units > 0x7fffffffL - 8) return MLA_ERR_UNSUPPORTED;
   c->a.nsplit = s;
   c->ws_bytes = mla_workspace_bytes(q->batch, q->q_len, q->heads, s);
@@ -328,10 +348,12 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
   plan->nsplit = c.a.nsplit;
   plan->waves_per_group = 2 * c.nb;
   plan->row_groups = c.groups;
-  plan->grid = c.a.nsplit * c.groups * q->batch * (c.kernel == 1 ? q->q_len : 1);
+  plan->grid = c.a.balance_units > 0 ? c.a.balance_units * c.groups
+                                      : c.a.nsplit * c.groups * q->batch * (c.kernel == 1 ? q->q_len : 1);
   plan->workspace_bytes = c.ws_bytes;
   plan->kernel = c.kernel;
   plan->row_blocks = c.nb;
+  plan->balanced = c.a.balance_units > 0 ? 1 : 0;
   return MLA_OK;
 }
 

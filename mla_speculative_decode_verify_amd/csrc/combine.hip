@@ -32,7 +32,8 @@ constexpr int kCombThreads = 256;
 // while those loads are in flight, so the whole merge costs about one
 // memory round trip. Splits beyond kMaxPer per lane are handled by further
 // rounds of the same loop. kCols = 64 suits many splits (8 splits per
-// wavefront load), kCols = 512 up to 32 (a wavefront per split).
+// wavefront load), kCols = 512 up to 32 (a wavefront per split); rows with
+// only a few splits take combine_rows_kernel below.
 template <int kCols>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   constexpr int kLanes = kCols / 8;                 // lanes per split slice
@@ -43,7 +44,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   __shared__ float den_lds[kGroups];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slice = blockIdx.x, row = blockIdx.y, b = blockIdx.z;
-  const int S = a.nsplit, R = a.rows;
+  const int S = a.nsplit, R = a.rows;  // S: the partials' split stride
+  // splits that hold this sequence's partials: all S, or its own count when
+  // the counts follow the lengths (the split kernel derives the same one)
+  const int Sb = a.balance_units > 0
+                     ? __builtin_amdgcn_readfirstlane(
+                           __shfl(balanced_split(a.seq_lens, a.batch, a.slot_stride, S, a.balance_units).count, b))
+                     : S;
   const int grp = tid / kLanes, cl = tid % kLanes;
   const int half = (slice * kCols + cl * 8) / 256;
   const size_t p0 = (size_t)b * S * R + row;  // partial output of split s: row p0 + s * R
@@ -53,7 +60,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
 
   // ---- max LSE over all splits (a separate, small pass: S floats)
   float mx = -INFINITY;
-  for (int s = tid; s < S; s += kCombThreads) mx = fmaxf(mx, a.part_lse[q0 + s]);
+  for (int s = tid; s < Sb; s += kCombThreads) mx = fmaxf(mx, a.part_lse[q0 + s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[wave] = mx;
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
 #pragma unroll
     for (int u = 0; u < kMaxPer; ++u) {
       const int s = s0 + u * kGroups;
-      const bool ok = s < S;
+      const bool ok = s < Sb;
       const size_t q = q0 + (ok ? s : 0);
       v[u] = ok ? *reinterpret_cast<const f16x8*>(po + (size_t)s * sstride) : f16x8{};
       ls[u] = ok ? a.part_lse[q] : -INFINITY;
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
 #pragma unroll
   for (int w = 1; w < kCombThreads / 64; ++w) mx = fmaxf(mx, red[w]);
   accumulate();
-  for (int s0 = grp + kMaxPer * kGroups; s0 < S; s0 += kMaxPer * kGroups) {
+  for (int s0 = grp + kMaxPer * kGroups; s0 < Sb; s0 += kMaxPer * kGroups) {
     load_round(s0);
     accumulate();
   }
@@ -113,6 +120,71 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   }
   if (slice == 0 && tid == 0 && a.lse)
     a.lse[(size_t)b * R + row] = tot > 0.f ? mx + fast_log2(tot) * kLn2 : -INFINITY;
+}
+
+// Merge with one wavefront per (sequence, query row), for rows with few
+// splits: lane l owns output columns 8 l .. 8 l + 7 (one 16-byte fp16 load
+// per split) and the wavefront walks the splits in rounds of kPer, all of a
+// round's loads in flight together. The base of the exponentials is the
+// running max of the LSEs seen so far; when a round raises it, the sums so
+// far are rescaled once (exact in real arithmetic: every weight is
+// exp(lse_s - M) for the final M). With at most kPer splits, as with the
+// library's split counts for most shapes, there is a single round and no
+// rescale. Four wavefronts per workgroup take four rows; the wavefronts
+// never synchronise, so those past the last row leave at once.
+__global__ __launch_bounds__(256) void combine_rows_kernel(Args a) {
+  constexpr int kPer = 8;
+  const int lane = (int)__lane_id();
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6), b = blockIdx.y;
+  const int S = a.nsplit, R = a.rows;  // S: the partials' split stride
+  if (row >= R) return;
+  const int Sb = a.balance_units > 0
+                     ? __builtin_amdgcn_readfirstlane(
+                           __shfl(balanced_split(a.seq_lens, a.batch, a.slot_stride, S, a.balance_units).count, b))
+                     : S;
+  const int half = lane >> 5;
+  const _Float16* po = a.part_o + ((size_t)b * S * R + row) * kDv + 8 * lane;
+  const size_t sstride = (size_t)R * kDv;
+  const size_t q0 = ((size_t)b * R + row) * S;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  float m = -INFINITY, den = 0.f;
+  for (int s0 = 0; s0 < Sb; s0 += kPer) {
+    f16x8 v[kPer];
+    float ls[kPer], sc[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int s = s0 + u;
+      const bool ok = s < Sb;
+      v[u] = ok ? *reinterpret_cast<const f16x8*>(po + (size_t)s * sstride) : f16x8{};
+      ls[u] = ok ? a.part_lse[q0 + s] : -INFINITY;
+      sc[u] = ok ? a.part_scale[(q0 + s) * 2 + half] : 0.f;
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) mx = fmaxf(mx, ls[u]);
+    if (mx != m && m != -INFINITY) {  // uniform: every lane holds the same LSEs
+      const float alpha = fast_exp2((m - mx) * kLog2e);
+      den *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    }
+    m = mx;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const float w = ls[u] == -INFINITY ? 0.f : fast_exp2((ls[u] - m) * kLog2e);  // m > -inf whenever ls is
+      den += w;
+      const float ws = w * sc[u];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(ws, (float)v[u][j], acc[j]);
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float* dst = a.out + ((size_t)b * R + row) * kDv + 8 * lane;
+  reinterpret_cast<f32x4*>(dst)[0] = f32x4{acc[0], acc[1], acc[2], acc[3]} * inv;
+  reinterpret_cast<f32x4*>(dst)[1] = f32x4{acc[4], acc[5], acc[6], acc[7]} * inv;
+  if (lane == 0 && a.lse) a.lse[(size_t)b * R + row] = den > 0.f ? m + fast_log2(den) * kLn2 : -INFINITY;
 }
 
 // One thread per (sequence, draft): walk the parent chain to the root.
@@ -145,7 +217,12 @@ __global__ void tree_mask_kernel(const int32_t* parents, int batch, int q_len, u
 }  // namespace
 
 hipError_t launch_combine(const Args& a, hipStream_t stream) {
-  if (a.nsplit <= 32) {
+  // one wavefront per row while its splits fit one or two rounds of loads
+  // (length-following counts stay far below their stride); a workgroup per
+  // row up to 32, per 64-column slice beyond
+  if (a.nsplit <= 8 || (a.balance_units > 0 && a.nsplit <= 32)) {
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((a.rows + 3) / 4, a.batch), dim3(256), 0, stream, a);
+  } else if (a.nsplit <= 32) {
     hipLaunchKernelGGL(combine_kernel<kDv>, dim3(1, a.rows, a.batch), dim3(kCombThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(combine_kernel<64>, dim3(kDv / 64, a.rows, a.batch), dim3(kCombThreads), 0, stream, a);

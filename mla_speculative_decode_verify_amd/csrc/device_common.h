@@ -110,4 +110,73 @@ __device__ __forceinline__ int xcd_unit(int units) {
 }
 inline unsigned xcd_grid(long units) { return (unsigned)(((units + kXcds - 1) / kXcds) * kXcds); }
 
+// Sum / max over the 64 lanes, every lane getting the result, in VALU
+// cross-lane moves only (no LDS permute): DPP swaps within quads, then
+// mirrors within 8- and 16-lane rows (each pairs every lane with one of the
+// other half, which is all a symmetric reduction needs), then the gfx950
+// 16- and 32-lane swaps.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i32(int v, Op op) {
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = op((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return op((int)b[0], (int)b[1]);
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return wave_reduce_i32(v, [](int x, int y) { return x + y; });
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  return wave_reduce_i32(v, [](int x, int y) { return max(x, y); });
+}
+
+// Split counts that follow the sequence lengths of a ragged batch (at most
+// 64 sequences, one per lane). Sequence b, with n_b positions clamped to
+// [0, slot_stride] and t_b = ceil(n_b / 32) tiles, gets
+//   S_b = min(ceil(t_b / T), cap_b), at least 1,  cap_b = min(smax, ceil(t_b / 4)),
+// where T is the smallest tile budget for which sum_b S_b <= units. Every
+// split then holds about T tiles whichever sequence it belongs to, so the
+// splits of a one-pass grid finish together instead of all waiting for the
+// longest sequence; cap_b keeps at least 4 tiles per split, as the uniform
+// rule does. sum_b S_b is non-increasing in T, and at most units already at
+// T = ceil(sum_b t_b / (units - batch)) (each S_b <= t_b / T + 1) when
+// units > batch, and at T = max_b t_b, where it equals the batch size; so a
+// binary search below the smaller bound finds T whenever units >= batch
+// (the host guarantees it). Computed from seq_lens alone, so the split and merge
+// kernels agree without a table in memory. All 64 lanes must call it; lane b
+// (< batch) gets S_b, the splits of sequences 0..b-1 in `first`, and its raw
+// seq_lens entry in `len`; every lane gets the sum in `total`.
+struct BalancedSplit {
+  int count, first, total, len;
+};
+__device__ __forceinline__ BalancedSplit balanced_split(const int32_t* seq_lens, int batch, int slot_stride,
+                                                        int smax, int units) {
+  const int lane = (int)__lane_id();
+  const bool live = lane < batch;
+  const int len = live ? seq_lens[lane] : 0;
+  const int n = min(max(len, 0), slot_stride);
+  const int t = (n + 31) / 32;
+  const int cap = live ? min(smax, max(1, (t + 3) / 4)) : 0;
+  auto count = [&](int T) { return live ? min(cap, max(1, (t + T - 1) / T)) : 0; };
+  const int tot = wave_sum_i32(t);
+  int lo = 1, hi = max(1, wave_max_i32(t));
+  if (units > batch) hi = min(hi, max(1, (tot + (units - batch) - 1) / (units - batch)));
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (wave_sum_i32(count(mid)) <= units) hi = mid;
+    else lo = mid + 1;
+  }
+  const int c = count(lo);
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  return BalancedSplit{c, incl - c, __shfl(incl, 63), len};
+}
+
 }  // namespace mla

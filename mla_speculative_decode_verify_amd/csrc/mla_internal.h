@@ -35,7 +35,10 @@ struct Args {
                             // split kernels start loading the slots of the split this implies
                             // before the true length arrives, and keep them if it matches
   int batch, q_len, heads, rows;  // rows = q_len * heads
-  int nsplit;
+  int nsplit;               // splits per sequence; with balance_units, their upper bound and
+                            // the partials' stride
+  int balance_units;        // > 0: per-sequence split counts follow the lengths
+                            // (balanced_split), with at most this many splits in all
   int row_groups;           // workgroups along the row axis (set at launch)
   int mask_kind;
   int topk;

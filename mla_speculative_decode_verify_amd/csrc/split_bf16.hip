@@ -152,7 +152,7 @@ __device__ __forceinline__ bf16x8 v_operand(const __bf16* vT0, int d) {
   return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int NB>
+template <int NB, bool kBalanced>
 __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   constexpr int NW = 2 * NB;
   // Fewest gather instructions any wave issues per tile: waiting until at
@@ -168,22 +168,40 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar wave index
   const int g = lane >> 4, li = lane & 15;
   const int half = wave & 1, blk = wave >> 1;
-  // unit = (b * nsplit + split) * row_groups + grp, in XCD-aware order
+  // unit = (k * row_groups + grp) in XCD-aware order, where k = b * nsplit +
+  // split (uniform counts) or the running split index over the batch
+  // (length-following counts, kBalanced)
   const int G = a.row_groups;
-  const int unit = xcd_unit(a.batch * a.nsplit * G);
+  const int unit = xcd_unit((kBalanced ? a.balance_units : a.batch * a.nsplit) * G);
   if (unit < 0) return;  // padding workgroup: uniform exit before any barrier
-  const int grp = unit % G, split = (unit / G) % a.nsplit, b = unit / (G * a.nsplit);
-  const int S = a.nsplit, R = a.rows;
+  const int grp = unit % G, k = unit / G;
+  int b, split, S, len = 0;  // S = splits of sequence b
+  if (kBalanced) {
+    // every wavefront derives the same schedule, so the exit is uniform
+    const BalancedSplit bs = balanced_split(a.seq_lens, a.batch, a.slot_stride, a.nsplit, a.balance_units);
+    if (k >= bs.total) return;
+    // wave-uniform values, kept in scalar registers
+    b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < a.batch && bs.first + bs.count <= k)));
+    split = __builtin_amdgcn_readfirstlane(k - __shfl(bs.first, b));
+    S = __builtin_amdgcn_readfirstlane(__shfl(bs.count, b));
+    len = __builtin_amdgcn_readfirstlane(__shfl(bs.len, b));
+  } else {
+    split = k % a.nsplit;
+    b = k / a.nsplit;
+    S = a.nsplit;
+  }
+  const int R = a.rows;
   const bool leader = (tid == 0) && (split == 0) && (grp == 0);
   const int32_t* slot_row = a.slots + (size_t)b * a.slot_stride;
 
   // ---- first batch of slot loads, issued before the sequence length is
   // known: they assume the split range that the host's length bound implies
   // and are used only if the true range turns out the same, so the slot
-  // loads no longer wait behind the length load
+  // loads no longer wait behind the length load (uniform counts only: with
+  // length-following counts the length is already known)
   constexpr int kBatch = NW * 64;  // slot loads per staging pass and unroll step
-  int lo_h, hi_h;
-  split_range(a.len_hint, S, split, lo_h, hi_h);
+  int lo_h = 0, hi_h = 0;
+  if (!kBalanced) split_range(a.len_hint, S, split, lo_h, hi_h);
   int v_h[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -192,7 +210,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   }
 
   // ---- sequence bounds and this split's key range
-  int n = a.seq_lens[b];
+  int n = kBalanced ? len : a.seq_lens[b];
   if (n < 0 || n > a.slot_stride) {
     if (leader) flag_error(a.err, MLA_DEVERR_SEQ_LEN);
     n = n < 0 ? 0 : a.slot_stride;
@@ -422,8 +440,11 @@ template <int NB>
 hipError_t launch_nb(const Args& a, int row_groups, hipStream_t stream) {
   Args b = a;
   b.row_groups = row_groups;
-  const long units = (long)a.batch * a.nsplit * row_groups;
-  hipLaunchKernelGGL(split_bf16_kernel<NB>, dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
+  const long units = (long)(a.balance_units > 0 ? a.balance_units : a.batch * a.nsplit) * row_groups;
+  if (a.balance_units > 0)
+    hipLaunchKernelGGL((split_bf16_kernel<NB, true>), dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
+  else
+    hipLaunchKernelGGL((split_bf16_kernel<NB, false>), dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
   return hipGetLastError();
 }
 

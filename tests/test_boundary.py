@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 12, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/mla_verify.h but not exported"
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
 
 
 def test_status_strings(L):
@@ -126,6 +126,25 @@ def test_plan_shapes(L):
     assert (p["waves_per_group"], p["row_groups"], p["row_blocks"]) == (10, 2, 5)
     p = B.plan(2, 1, 1, 10, nsplit=1)
     assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 2
+
+
+def test_plan_balanced_splits(L):
+    # ragged batch, library-chosen splits: counts follow the lengths. 9 row
+    # groups of 4 blocks -> 28 splits in one pass of 256 CUs (252 workgroups);
+    # the partial stride is what one sequence can take: 28 - 7 = 21
+    p = B.plan(8, 9, 64, 26681)
+    assert (p["balanced"], p["nsplit"], p["row_groups"], p["grid"]) == (1, 21, 9, 252)
+    assert p["workspace_bytes"] == 8 * 21 * 576 * 1036
+    # the stride never exceeds ceil(tiles / 4) of the longest allowed sequence
+    p = B.plan(2, 9, 8, 300)                   # 10 tiles -> at most 3 splits each, 6 in all
+    assert (p["balanced"], p["nsplit"], p["grid"]) == (1, 3, 6)
+    # uniform counts: an explicit nsplit, one sequence, more than 64, or too
+    # many sequences for the grid
+    assert B.plan(8, 9, 64, 26681, nsplit=3)["balanced"] == 0
+    assert B.plan(1, 9, 8, 65545)["balanced"] == 0
+    assert B.plan(65, 1, 8, 4096)["balanced"] == 0
+    assert B.plan(30, 9, 64, 4096)["balanced"] == 0   # 28 units < 30 sequences
+    assert B.plan(2, 9, 8, 100)["balanced"] == 0      # 4 tiles: one split each anyway
 
 
 def test_plan_shapes_fp8_topk(L):

@@ -80,6 +80,20 @@ def test_edge_shapes(q_len, heads, prefixes, mask):
     _check(w, [1, 2, 5, 300, 1024, 0])
 
 
+@pytest.mark.parametrize("heads,prefixes,mask", [
+    (8, [0, 40000], "causal"),        # one sequence takes nearly all splits, the other one
+    (8, [int(x) for x in np.random.default_rng(7).integers(0, 3000, size=64)], "tree"),  # 64: one per lane
+    (64, [5000, 300, 12000], "tree"),  # 9 row groups: 28 splits shared by 3 sequences
+])
+def test_length_following_splits(heads, prefixes, mask):
+    # library-chosen splits on a ragged batch: the split counts follow the
+    # lengths (derived on the device by the split and the merge kernels)
+    w = I.make_verify(f"balanced_h{heads}_b{len(prefixes)}", batch=len(prefixes), q_len=9, heads=heads,
+                      prefixes=prefixes, seed=50 + len(prefixes), layout="random", mask=mask)
+    assert B.plan(w.batch, w.q_len, w.heads, w.slot_stride, mask=mask)["balanced"] == 1
+    _check(w, [0], heads=None if heads == 8 else [0, 40, 63])
+
+
 def test_repeat_bitwise_and_pool_permutation():
     w = I.make_verify("perm", batch=2, q_len=9, heads=8, prefixes=[700, 1500], seed=31, layout="random",
                       mask="tree")
@@ -129,6 +143,7 @@ def test_tree_mask_device_bit_exact():
     ("c3_64k", 0),
     ("c3_64k", 40),
     ("c2", 0),
+    ("c4", 0),        # ragged batch: split counts that follow the lengths
 ])
 def test_split_and_combine_stages_equal_full_call(name, nsplit):
     # The two entry points of the split and the merge, called in turn, give
