@@ -189,14 +189,20 @@ int mla_verify_combine(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t
 int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_desc, int nsplit,
              mla_plan_t* plan);
 
-/* Split count the library picks when nsplit <= 0: a pure function of the
- * shape and the CU count, so it is deterministic and safe under graph
- * capture. At most one split-kernel workgroup per CU and at least 128
- * positions per split; for a bf16 cache, the fewest splits that keep the
- * largest per-split count of 32-position tiles. max_seq_len is the longest sequence for a bf16 cache and the
- * top-k list length for an fp8 cache (each query's list is split). ("How One Environment Variable Unlocked 3x Throughput", section
- * "The Occupancy Revelation": a small per-rank head count shrinks the grid
- * until the machine starves, and more splits refill it.) */
+/* Split count the library picks when nsplit <= 0 (one count for every
+ * sequence): a pure function of the shape and the CU count, so it is
+ * deterministic and safe under graph capture. At most one split-kernel
+ * workgroup per CU. For a bf16 cache, the count s that minimises a cost
+ * model of the verify kernel measured on MI355X: ceil(tiles / s) 32-position
+ * tiles at 2 us each for the slowest split, plus, when s > 1, 6 us for the
+ * merge kernel and the partials (2 x 1036 bytes per split and query row) at
+ * 3.5 TB/s; the fewest splits on ties. For an fp8 cache, as many as fit,
+ * with at least 128 list entries per split. max_seq_len is the longest
+ * sequence for a bf16 cache and the top-k list length for an fp8 cache
+ * (each query's list is split). ("How One Environment Variable Unlocked 3x
+ * Throughput", section "The Occupancy Revelation": a small per-rank head
+ * count shrinks the grid until the machine starves, and more splits refill
+ * it.) */
 int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus);
 
 /* Bytes of split partials one call needs: batch * nsplit * q_len * heads *

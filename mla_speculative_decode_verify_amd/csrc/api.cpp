@@ -148,6 +148,11 @@ void row_layout(int batch, int q_len, int heads, int kv_dtype, int* nb, int* gro
   }
 }
 
+// Measured time of one 32-position tile of the bf16 verify loop (both head
+// counts run at about this pace), for the split-count cost model.
+constexpr double kTileUs = 2.0;
+constexpr double kMergeUs = 6.0;  // the merge kernel of a call with several splits
+
 // `keys` = positions per key set: the longest sequence (bf16 verify) or the
 // top-k list length (fp8 sparse).
 int choose_nsplit_impl(int batch, int q_len, int heads, int keys, int kv_dtype, int num_cus) {
@@ -157,18 +162,30 @@ int choose_nsplit_impl(int batch, int q_len, int heads, int keys, int kv_dtype, 
   row_layout(batch, q_len, heads, kv_dtype, &nb, &groups, &key_sets);
   const long wgs_per_split = key_sets * groups;
   // One workgroup per CU at most (a split kernel workgroup fills a CU), so
-  // the grid runs in a single wave; never fewer than 4 tiles (128 keys) per
-  // split.
-  long s = std::max<long>(1, num_cus / wgs_per_split);
-  const long cap = std::max<long>(1, ((long)keys + 127) / 128);
-  s = std::min(s, cap);
+  // the grid runs in a single pass.
+  const long one_pass = std::max<long>(1, num_cus / wgs_per_split);
+  long s = one_pass;
   if (kv_dtype == MLA_KV_BF16) {
-    // The verify kernel gives each split whole 32-position tiles, so the
-    // slowest split runs ceil(tiles / s) of them: take the fewest splits
-    // with that same maximum (fewer partials to write and merge).
+    // Cost model (microseconds, from measurements of the verify kernel on
+    // MI355X): the slowest split runs ceil(tiles / s) 32-position tiles at
+    // about 2 us each (a latency-bound chain), and every split adds its
+    // partials, 1036 bytes per query row written and then read by the
+    // merge, at about 3.5 TB/s, and more than one split costs the merge
+    // kernel (about 6 us). The cheapest s wins, the fewest on ties.
     const long tiles = std::max<long>(1, ((long)keys + 31) / 32);
-    const long per = (tiles + s - 1) / s;
-    s = (tiles + per - 1) / per;
+    const double part_us = 2.0 * 1036.0 * (double)batch * q_len * heads / 3.5e6;
+    double best = 0.0;
+    for (long c = 1; c <= std::min(one_pass, tiles); ++c) {
+      const double cost =
+          (double)((tiles + c - 1) / c) * kTileUs + (c > 1 ? (double)c * part_us + kMergeUs : 0.0);
+      if (c == 1 || cost < best) {
+        best = cost;
+        s = c;
+      }
+    }
+  } else {
+    // fp8 top-k lists: never fewer than 128 list entries per split
+    s = std::min(s, std::max<long>(1, ((long)keys + 127) / 128));
   }
   s = std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
   return (int)s;

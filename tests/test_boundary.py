@@ -104,13 +104,17 @@ def test_choose_nsplit_rules(L):
     # one tensor-parallel rank's share: H=8, q_len 9 -> 72 rows, one row group
     # 2049 tiles of 32 over at most 256 splits: 9 tiles for the slowest,
     # and 228 splits already achieve that
+    # (cost: 2 us per tile of the slowest split, plus 6 us and 2 x 1036 B at
+    # 3.5 TB/s per split and row once there are several splits)
     assert B.choose_nsplit(1, 9, 8, 65545, num_cus=256) == 228
     assert B.choose_nsplit(1, 9, 8, 65536, num_cus=256) == 256      # 2048 tiles: 8 each
-    assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 129      # capped: >= 128 keys per split
+    assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 171      # 3 tiles each: 6 + 6 + 7.3 us
+    assert B.choose_nsplit(1, 9, 8, 265, num_cus=256) == 9          # one tile each
     # 9 row groups: at most 28 splits (252 workgroups, one wave); 129 tiles
     # need 5 per split, which 26 splits give
     assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 26
-    assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 1
+    assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 1          # 4 tiles: 8 us alone, 8.2 us split
+    assert B.choose_nsplit(1, 9, 8, 32, num_cus=256) == 1
     assert B.choose_nsplit(32, 1, 64, 2048, kv_dtype=B.MLA_KV_FP8_E4M3, num_cus=256) == 8
     for args in [(0, 9, 8, 10, 0, 256), (1, 9, 8, -1, 0, 256), (1, 9, 8, 10, 5, 256), (1, 9, 8, 10, 0, 0)]:
         assert L.mla_choose_nsplit(*args) == B.MLA_ERR_INVALID_ARG
