@@ -192,22 +192,26 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
 /* Split count the library picks when nsplit <= 0 (one count for every
  * sequence): a pure function of the shape and the CU count, so it is
  * deterministic and safe under graph capture. At most one split-kernel
- * workgroup per CU. For a bf16 cache, the count s that minimises a cost
- * model of the verify kernel measured on MI355X: ceil(tiles / s) 32-position
- * tiles at 2 us each for the slowest split, plus, when s > 1, 6 us for the
- * merge kernel and the partials (2 x 1036 bytes per split and query row) at
- * 3.5 TB/s; the fewest splits on ties. For an fp8 cache, as many as fit,
- * with at least 128 list entries per split. max_seq_len is the longest
- * sequence for a bf16 cache and the top-k list length for an fp8 cache
- * (each query's list is split). ("How One Environment Variable Unlocked 3x
- * Throughput", section "The Occupancy Revelation": a small per-rank head
- * count shrinks the grid until the machine starves, and more splits refill
- * it.) */
+ * workgroup per CU. For a bf16 cache the library picks the query rows per
+ * workgroup (up to six 16-row blocks; more rows are dealt to several
+ * workgroups that gather the same keys) together with the count s, by a
+ * cost model fitted to cold-cache calls on MI355X: about 1.86 us per
+ * 32-position tile of the slowest split (2.21 us with six blocks per
+ * workgroup), 8 us fixed (11.4 us with six blocks), and, when s > 1, 4 us
+ * for the merge plus 0.49 us per MB of partials (1036 bytes per split and
+ * query row, written and read back); the cheapest wins, the fewest splits on
+ * ties. For an fp8 cache, as many as fit, with at least 128 list entries
+ * per split. max_seq_len is the longest sequence for a bf16 cache and the
+ * top-k list length for an fp8 cache (each query's list is split). ("How
+ * One Environment Variable Unlocked 3x Throughput", section "The Occupancy
+ * Revelation": a small per-rank head count shrinks the grid until the
+ * machine starves, and more splits refill it.) */
 int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_dtype, int num_cus);
 
 /* Bytes of split partials one call needs: batch * nsplit * q_len * heads *
  * (512 * 2 + 12) (fp16 partial output, its two power-of-two scales and the
- * fp32 LSE per split and row), or 0 for nsplit <= 1. */
+ * fp32 LSE per split and row) plus batch * 4 (each sequence's split count
+ * when the counts follow the lengths), or 0 for nsplit <= 1. */
 size_t mla_workspace_bytes(int batch, int q_len, int heads, int nsplit);
 
 /* Make the workspace of (current device, stream) at least `bytes` long and

@@ -109,86 +109,112 @@ int workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
 }
 
 // ----------------------------------------------------------------- planning
-// Query rows are cut into 16-row blocks; a workgroup serves `nb` blocks with
-// two wavefronts each (split_bf16.hip), at most 5 blocks (10 wavefronts).
-// Pick the grouping with the least padded work, preferring 4 blocks (two
-// wavefronts per SIMD) on ties.
-void choose_row_groups(int rows, int* nb, int* groups) {
-  const int blocks = (rows + 15) / 16;
-  if (blocks <= 5) {
-    *nb = blocks;
-    *groups = 1;
-    return;
-  }
-  const int g4 = (blocks + 3) / 4, g5 = (blocks + 4) / 5;
-  if (g5 * 5 < g4 * 4) {
-    *nb = 5;
-    *groups = g5;
-  } else {
-    *nb = 4;
-    *groups = g4;
-  }
+// Query rows are cut into 16-row blocks; a bf16 split workgroup serves `nb`
+// blocks with two wavefronts each (split_bf16.hip), at most 6 blocks (12
+// wavefronts, three per SIMD). Rows of one sequence that do not fit one
+// workgroup are dealt to `groups` workgroups, each gathering the same keys.
+//
+// Cost model of one bf16 call (microseconds; a least-squares fit to 23
+// cold-cache call times on MI355X at H=8 and H=64 with 4, 5 and 6 blocks per
+// workgroup and 1 to 74 tiles per split, residuals within 2 us): a
+// 32-position tile of the slowest split costs about 1.86 us with up to 5
+// blocks per workgroup and 2.21 us with 6 (three wavefronts per SIMD share
+// its MFMA and LDS instead of two), a call has about 8 us of fixed cost
+// (11.4 us with 6 blocks: more query rows to load and partial rows to
+// store per workgroup); with several splits the merge kernel adds about
+// 4 us, and every split's partials (1036 bytes per query row, written and
+// read back) about 0.49 us per MB.
+constexpr double kTileUs[7] = {0.0, 1.86, 1.86, 1.86, 1.86, 1.86, 2.21};  // by blocks per workgroup
+constexpr double kFixedUs[7] = {0.0, 8.1, 8.1, 8.1, 8.1, 8.1, 11.4};
+constexpr double kPartUsPerByte = 0.49e-6;
+constexpr double kMergeUs = 4.0;
+constexpr int kMaxBlocks = 6;
+
+double bf16_cost_us(int nb, long wgs_per_split, long tiles, long s, long rows_total, int num_cus) {
+  const long passes = (wgs_per_split * s + num_cus - 1) / num_cus;
+  double t = kFixedUs[nb] + (double)(passes * ((tiles + s - 1) / s)) * kTileUs[nb];
+  if (s > 1) t += kMergeUs + kPartUsPerByte * 1036.0 * (double)rows_total * (double)s;
+  return t;
 }
 
-// Workgroups along the row axis and independent key sets per split: the
-// bf16 verify path groups all q_len * heads rows of a sequence (they share
-// its keys); the fp8 top-k path groups the heads of one query (each query
-// has its own key list), so its key sets are batch * q_len.
-// The fp8 kernel converts tiles in registers and spills with 5 blocks, so
-// its groups hold at most 4 blocks.
-void row_layout(int batch, int q_len, int heads, int kv_dtype, int* nb, int* groups, long* key_sets) {
+// Best split count for `nb` blocks in `groups` workgroups per key set: one
+// workgroup per CU at most (a split workgroup fills a CU), so the grid runs
+// in a single pass; the cheapest count wins, the fewest on ties.
+long bf16_best_split(int nb, long wgs_per_split, long tiles, long rows_total, int num_cus, double* cost) {
+  const long one_pass = std::max<long>(1, num_cus / wgs_per_split);
+  long s = 1;
+  double best = 0.0;
+  for (long c = 1; c <= std::min(one_pass, tiles); ++c) {
+    const double t = bf16_cost_us(nb, wgs_per_split, tiles, c, rows_total, num_cus);
+    if (c == 1 || t < best) {
+      best = t;
+      s = c;
+    }
+  }
+  *cost = best;
+  return s;
+}
+
+struct Layout {
+  int nb = 1, groups = 1;
+  int nsplit = 1;
+  long key_sets = 1;
+};
+
+// Row grouping and split count. bf16 verify: all q_len * heads rows of a
+// sequence share its keys, so they form the key set; up to 6 blocks fit one
+// workgroup, else the blocks-per-workgroup and split count come jointly from
+// the cost model. fp8 top-k: the heads of one query share its list, so the
+// key sets are batch * q_len; that kernel converts tiles in registers and
+// spills with 5 blocks, so its groups hold at most 4 blocks and its splits
+// never hold fewer than 128 list entries. `keys` = positions per key set
+// (the longest sequence, or the top-k list length); `nsplit` > 0 is kept.
+Layout plan_layout(int batch, int q_len, int heads, int keys, int kv_dtype, int num_cus, int nsplit) {
+  Layout L;
+  num_cus = std::max(1, num_cus);
   if (kv_dtype == MLA_KV_FP8_E4M3) {
     const int blocks = (heads + 15) / 16;
-    *nb = std::min(blocks, 4);
-    *groups = (blocks + *nb - 1) / *nb;
-    *key_sets = (long)batch * q_len;
-  } else {
-    choose_row_groups(q_len * heads, nb, groups);
-    *key_sets = batch;
+    L.nb = std::min(blocks, 4);
+    L.groups = (blocks + L.nb - 1) / L.nb;
+    L.key_sets = (long)batch * q_len;
+    long s = nsplit;
+    if (s <= 0) {
+      s = std::max<long>(1, num_cus / (L.key_sets * L.groups));
+      s = std::min(s, std::max<long>(1, ((long)keys + 127) / 128));
+    }
+    L.nsplit = (int)std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
+    return L;
   }
+  const int rows = q_len * heads;
+  const int blocks = (rows + 15) / 16;
+  const long tiles = std::max<long>(1, ((long)keys + 31) / 32);
+  const long rows_total = (long)batch * rows;
+  L.key_sets = batch;
+  double best = 0.0;
+  bool have = false;
+  for (int nb = 1; nb <= kMaxBlocks; ++nb) {
+    // one workgroup when the blocks fit; otherwise 4 to 6 blocks per group
+    if (blocks <= kMaxBlocks ? nb != blocks : nb < 4) continue;
+    const int groups = (blocks + nb - 1) / nb;
+    const long wgs = (long)batch * groups;
+    double cost = 0.0;
+    long s = nsplit;
+    if (s > 0) cost = bf16_cost_us(nb, wgs, tiles, s, rows_total, num_cus);
+    else s = bf16_best_split(nb, wgs, tiles, rows_total, num_cus, &cost);
+    if (!have || cost < best) {
+      have = true;
+      best = cost;
+      L.nb = nb;
+      L.groups = groups;
+      L.nsplit = (int)std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
+    }
+  }
+  return L;
 }
 
-// Measured time of one 32-position tile of the bf16 verify loop (both head
-// counts run at about this pace), for the split-count cost model.
-constexpr double kTileUs = 2.0;
-constexpr double kMergeUs = 6.0;  // the merge kernel of a call with several splits
-
-// `keys` = positions per key set: the longest sequence (bf16 verify) or the
-// top-k list length (fp8 sparse).
 int choose_nsplit_impl(int batch, int q_len, int heads, int keys, int kv_dtype, int num_cus) {
   if (batch < 1 || q_len < 1 || heads < 1 || num_cus < 1) return 1;
-  int nb, groups;
-  long key_sets;
-  row_layout(batch, q_len, heads, kv_dtype, &nb, &groups, &key_sets);
-  const long wgs_per_split = key_sets * groups;
-  // One workgroup per CU at most (a split kernel workgroup fills a CU), so
-  // the grid runs in a single pass.
-  const long one_pass = std::max<long>(1, num_cus / wgs_per_split);
-  long s = one_pass;
-  if (kv_dtype == MLA_KV_BF16) {
-    // Cost model (microseconds, from measurements of the verify kernel on
-    // MI355X): the slowest split runs ceil(tiles / s) 32-position tiles at
-    // about 2 us each (a latency-bound chain), and every split adds its
-    // partials, 1036 bytes per query row written and then read by the
-    // merge, at about 3.5 TB/s, and more than one split costs the merge
-    // kernel (about 6 us). The cheapest s wins, the fewest on ties.
-    const long tiles = std::max<long>(1, ((long)keys + 31) / 32);
-    const double part_us = 2.0 * 1036.0 * (double)batch * q_len * heads / 3.5e6;
-    double best = 0.0;
-    for (long c = 1; c <= std::min(one_pass, tiles); ++c) {
-      const double cost =
-          (double)((tiles + c - 1) / c) * kTileUs + (c > 1 ? (double)c * part_us + kMergeUs : 0.0);
-      if (c == 1 || cost < best) {
-        best = cost;
-        s = c;
-      }
-    }
-  } else {
-    // fp8 top-k lists: never fewer than 128 list entries per split
-    s = std::min(s, std::max<long>(1, ((long)keys + 127) / 128));
-  }
-  s = std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
-  return (int)s;
+  return plan_layout(batch, q_len, heads, keys, kv_dtype, num_cus, 0).nsplit;
 }
 
 struct Call {
@@ -234,13 +260,15 @@ int validate(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, co
 }
 
 int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsplit, int num_cus, Call* c) {
-  long key_sets = 0;
-  row_layout(q->batch, q->q_len, q->heads, kv->dtype, &c->nb, &c->groups, &key_sets);
-  if (key_sets > 65535) return MLA_ERR_UNSUPPORTED;
   c->kernel = kv->dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
   const int maxlen = kv->max_seq_len > 0 ? kv->max_seq_len : kv->slot_stride;
   const int seqlen_for_split = c->kernel == 1 ? std::min(maxlen, m->topk) : maxlen;
-  int s = nsplit > 0 ? nsplit : choose_nsplit_impl(q->batch, q->q_len, q->heads, seqlen_for_split, kv->dtype, num_cus);
+  const Layout L = plan_layout(q->batch, q->q_len, q->heads, seqlen_for_split, kv->dtype, num_cus, nsplit);
+  const long key_sets = L.key_sets;
+  if (key_sets > 65535) return MLA_ERR_UNSUPPORTED;
+  c->nb = L.nb;
+  c->groups = L.groups;
+  int s = L.nsplit;
   if (s > MLA_MAX_NSPLIT) return MLA_ERR_INVALID_ARG;
   c->a.balance_units = 0;
   if (nsplit <= 0 && c->kernel == 0 && q->batch >= 2 && q->batch <= kBalanceMaxBatch) {
@@ -283,6 +311,7 @@ void fill_args(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, 
   a.part_o = nullptr;
   a.part_lse = nullptr;
   a.part_scale = nullptr;
+  a.part_count = nullptr;
   a.err = nullptr;
   a.zero_row = nullptr;
   a.pool_rows = kv->pool_rows;
@@ -321,6 +350,7 @@ int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const i
     c.a.part_o = reinterpret_cast<_Float16*>(base);
     c.a.part_lse = reinterpret_cast<float*>(base + P * kDv * sizeof(_Float16));
     c.a.part_scale = c.a.part_lse + P;
+    c.a.part_count = reinterpret_cast<int32_t*>(c.a.part_scale + 2 * P);
   }
   if (stages & kSplit) {
     hipError_t e = c.kernel == 0 ? mla::launch_split_bf16(c.a, c.nb, c.groups, stream)
@@ -382,7 +412,8 @@ int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_d
 
 size_t mla_workspace_bytes(int batch, int q_len, int heads, int nsplit) {
   if (batch < 1 || q_len < 1 || heads < 1 || nsplit <= 1) return 0;
-  return (size_t)batch * nsplit * q_len * heads * (kDv * sizeof(_Float16) + 3 * sizeof(float));
+  return (size_t)batch * nsplit * q_len * heads * (kDv * sizeof(_Float16) + 3 * sizeof(float)) +
+         (size_t)batch * sizeof(int32_t);
 }
 
 int mla_reserve_workspace(size_t bytes, hipStream_t stream) {

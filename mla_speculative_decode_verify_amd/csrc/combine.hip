@@ -21,6 +21,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kCombThreads = 256;
 
+// Splits holding sequence b's partials: the stride S, or, when the counts
+// follow the lengths, the count the split kernel recorded (kept in [0, S]).
+__device__ __forceinline__ int split_count(const Args& a, int b) {
+  if (a.balance_units <= 0) return a.nsplit;
+  return __builtin_amdgcn_readfirstlane(min(max(a.part_count[b], 0), a.nsplit));
+}
+
 // Partials are fp16 rows of 512 columns with a power-of-two multiplier per
 // 256-column half (stored by the split kernels), plus an fp32 LSE.
 //
@@ -46,11 +53,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   const int slice = blockIdx.x, row = blockIdx.y, b = blockIdx.z;
   const int S = a.nsplit, R = a.rows;  // S: the partials' split stride
   // splits that hold this sequence's partials: all S, or its own count when
-  // the counts follow the lengths (the split kernel derives the same one)
-  const int Sb = a.balance_units > 0
-                     ? __builtin_amdgcn_readfirstlane(
-                           __shfl(balanced_split(a.seq_lens, a.batch, a.slot_stride, S, a.balance_units).count, b))
-                     : S;
+  // the counts follow the lengths (recorded by the split kernel)
+  const int Sb = split_count(a, b);
   const int grp = tid / kLanes, cl = tid % kLanes;
   const int half = (slice * kCols + cl * 8) / 256;
   const size_t p0 = (size_t)b * S * R + row;  // partial output of split s: row p0 + s * R
@@ -58,17 +62,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
   const _Float16* po = a.part_o + p0 * kDv + slice * kCols + cl * 8;
   const size_t sstride = (size_t)R * kDv;
 
-  // ---- max LSE over all splits (a separate, small pass: S floats)
-  float mx = -INFINITY;
-  for (int s = tid; s < Sb; s += kCombThreads) mx = fmaxf(mx, a.part_lse[q0 + s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) red[wave] = mx;
-
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   float den = 0.f;  // this lane's share of sum_s w_s (counted once per split: by lane cl == 0)
+  float mx = -INFINITY;  // max LSE over the splits
   f16x8 v[kMaxPer];
   float ls[kMaxPer], sc[kMaxPer];
   auto load_round = [&](int s0) {
@@ -92,9 +90,20 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Args a) {
       for (int j = 0; j < 8; ++j) acc[j] = fmaf(ws, (float)v[u][j], acc[j]);
     }
   };
-  // first round's loads are issued before the barrier that publishes the
-  // max, so they fly while it is reduced; every thread reaches the barrier
+  // The first round's loads are issued first. When one round covers every
+  // split, its LSEs are all the max needs, so the max costs no extra memory
+  // round trip; otherwise a separate pass reads all S LSEs while the first
+  // round's loads are in flight. Every thread reaches the barrier.
   load_round(grp);
+  if (Sb <= kMaxPer * kGroups) {
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) mx = fmaxf(mx, ls[u]);
+  } else {
+    for (int s = tid; s < Sb; s += kCombThreads) mx = fmaxf(mx, a.part_lse[q0 + s]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
   mx = red[0];
 #pragma unroll
@@ -138,10 +147,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(Args a) {
   const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6), b = blockIdx.y;
   const int S = a.nsplit, R = a.rows;  // S: the partials' split stride
   if (row >= R) return;
-  const int Sb = a.balance_units > 0
-                     ? __builtin_amdgcn_readfirstlane(
-                           __shfl(balanced_split(a.seq_lens, a.batch, a.slot_stride, S, a.balance_units).count, b))
-                     : S;
+  const int Sb = split_count(a, b);
   const int half = lane >> 5;
   const _Float16* po = a.part_o + ((size_t)b * S * R + row) * kDv + 8 * lane;
   const size_t sstride = (size_t)R * kDv;
@@ -217,10 +223,11 @@ __global__ void tree_mask_kernel(const int32_t* parents, int batch, int q_len, u
 }  // namespace
 
 hipError_t launch_combine(const Args& a, hipStream_t stream) {
-  // one wavefront per row while its splits fit one or two rounds of loads
-  // (length-following counts stay far below their stride); a workgroup per
-  // row up to 32, per 64-column slice beyond
-  if (a.nsplit <= 8 || (a.balance_units > 0 && a.nsplit <= 32)) {
+  // one wavefront per row while its splits fit a few rounds of loads
+  // (length-following counts stay far below their stride, and a workgroup
+  // per row and slice would mostly idle); a workgroup per row up to 32
+  // splits, per 64-column slice beyond
+  if (a.nsplit <= 8 || (a.balance_units > 0 && a.nsplit <= 64)) {
     hipLaunchKernelGGL(combine_rows_kernel, dim3((a.rows + 3) / 4, a.batch), dim3(256), 0, stream, a);
   } else if (a.nsplit <= 32) {
     hipLaunchKernelGGL(combine_kernel<kDv>, dim3(1, a.rows, a.batch), dim3(kCombThreads), 0, stream, a);

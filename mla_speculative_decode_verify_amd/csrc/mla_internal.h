@@ -27,6 +27,8 @@ struct Args {
   _Float16* part_o;         // [batch, nsplit, rows, 512] fp16, times part_scale per 256-column half
   float* part_lse;          // [batch, rows, nsplit]
   float* part_scale;        // [batch, rows, nsplit, 2] power-of-two multipliers of part_o
+  int32_t* part_count;      // [batch] splits holding partials, written by the split kernel
+                            // when the counts follow the lengths (balance_units > 0)
   unsigned* err;            // device error flag word
   const void* zero_row;     // >= 1152 zero bytes, read in place of masked / invalid cache rows
   int64_t pool_rows;

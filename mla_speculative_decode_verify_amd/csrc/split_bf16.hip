@@ -192,6 +192,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   }
   const int R = a.rows;
   const bool leader = (tid == 0) && (split == 0) && (grp == 0);
+  // the merge reads each sequence's split count from the workspace instead
+  // of deriving the schedule again in every one of its workgroups
+  if (kBalanced && leader) a.part_count[b] = S;
   const int32_t* slot_row = a.slots + (size_t)b * a.slot_stride;
 
   // ---- first batch of slot loads, issued before the sequence length is
@@ -457,6 +460,7 @@ hipError_t launch_split_bf16(const Args& a, int blocks, int row_groups, hipStrea
     case 3: return launch_nb<3>(a, row_groups, stream);
     case 4: return launch_nb<4>(a, row_groups, stream);
     case 5: return launch_nb<5>(a, row_groups, stream);
+    case 6: return launch_nb<6>(a, row_groups, stream);
     default: return hipErrorInvalidValue;
   }
 }

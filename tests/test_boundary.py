@@ -104,16 +104,28 @@ def test_choose_nsplit_rules(L):
     # one tensor-parallel rank's share: H=8, q_len 9 -> 72 rows, one row group
     # 2049 tiles of 32 over at most 256 splits: 9 tiles for the slowest,
     # and 228 splits already achieve that
-    # (cost: 2 us per tile of the slowest split, plus 6 us and 2 x 1036 B at
-    # 3.5 TB/s per split and row once there are several splits)
+    # (cost: 1.86 us per tile of the slowest split and 8.1 us fixed, plus
+    # 4 us and 0.49 us per MB of partials, 1036 B per split and row, once
+    # there are several splits)
     assert B.choose_nsplit(1, 9, 8, 65545, num_cus=256) == 228
     assert B.choose_nsplit(1, 9, 8, 65536, num_cus=256) == 256      # 2048 tiles: 8 each
-    assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 171      # 3 tiles each: 6 + 6 + 7.3 us
+    assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 171      # 3 tiles each: 5.6 + 6.3 us, 4 tiles: 7.4 + 4.7
     assert B.choose_nsplit(1, 9, 8, 265, num_cus=256) == 9          # one tile each
-    # 9 row groups: at most 28 splits (252 workgroups, one wave); 129 tiles
-    # need 5 per split, which 26 splits give
+    # H=64 short: 9 row groups of 4 blocks, at most 28 splits (252
+    # workgroups, one wave); 129 tiles need 5 per split, which 26 splits give
     assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 26
-    assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 1          # 4 tiles: 8 us alone, 8.2 us split
+    p = B.plan(1, 9, 64, 4105)
+    assert (p["row_blocks"], p["row_groups"], p["grid"]) == (4, 9, 234)
+    # H=64 at 16k: 8 row groups of 5 blocks (one group half empty) fit 32
+    # splits; 31 give 17 tiles each against 19 for 9 groups of 4
+    p = B.plan(1, 9, 64, 16393)
+    assert (p["nsplit"], p["row_blocks"], p["row_groups"], p["grid"]) == (31, 5, 8, 248)
+    # H=64 at 64k: 6 row groups of 6 blocks read each key 6 times instead of
+    # 9; at most 42 splits, 49 tiles each against 74 (2.21 us per tile
+    # instead of 1.86, 3.3 us more fixed cost)
+    p = B.plan(1, 9, 64, 65545)
+    assert (p["nsplit"], p["row_blocks"], p["row_groups"], p["grid"]) == (42, 6, 6, 252)
+    assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 4          # 4 tiles: 7.4 us alone, 1.9 + 4.1 split
     assert B.choose_nsplit(1, 9, 8, 32, num_cus=256) == 1
     assert B.choose_nsplit(32, 1, 64, 2048, kv_dtype=B.MLA_KV_FP8_E4M3, num_cus=256) == 8
     for args in [(0, 9, 8, 10, 0, 256), (1, 9, 8, -1, 0, 256), (1, 9, 8, 10, 5, 256), (1, 9, 8, 10, 0, 0)]:
@@ -123,22 +135,24 @@ def test_choose_nsplit_rules(L):
 def test_plan_shapes(L):
     p = B.plan(1, 9, 8, 16393, nsplit=64)      # 72 rows: 5 blocks of 16, two wavefronts each
     assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (64, 10, 1, 64, 5)
-    assert p["workspace_bytes"] == 64 * 72 * 1036
+    assert p["workspace_bytes"] == 64 * 72 * 1036 + 4
     p = B.plan(1, 9, 64, 4105, nsplit=16)
     assert (p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (8, 9, 144, 4)
-    p = B.plan(1, 9, 16, 4105, nsplit=16)      # 144 rows = 9 blocks: groups of 5 + 4
-    assert (p["waves_per_group"], p["row_groups"], p["row_blocks"]) == (10, 2, 5)
+    # 144 rows = 9 blocks: one pass of the grid either way, so 3 groups of 4
+    # (the smaller workgroups start and finish sooner)
+    p = B.plan(1, 9, 16, 4105, nsplit=16)
+    assert (p["waves_per_group"], p["row_groups"], p["row_blocks"]) == (8, 3, 4)
     p = B.plan(2, 1, 1, 10, nsplit=1)
     assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 2
 
 
 def test_plan_balanced_splits(L):
-    # ragged batch, library-chosen splits: counts follow the lengths. 9 row
-    # groups of 4 blocks -> 28 splits in one pass of 256 CUs (252 workgroups);
-    # the partial stride is what one sequence can take: 28 - 7 = 21
+    # ragged batch, library-chosen splits: counts follow the lengths. 6 row
+    # groups of 6 blocks -> 42 splits in one pass of 256 CUs (252 workgroups);
+    # the partial stride is what one sequence can take: 42 - 7 = 35
     p = B.plan(8, 9, 64, 26681)
-    assert (p["balanced"], p["nsplit"], p["row_groups"], p["grid"]) == (1, 21, 9, 252)
-    assert p["workspace_bytes"] == 8 * 21 * 576 * 1036
+    assert (p["balanced"], p["nsplit"], p["row_groups"], p["row_blocks"], p["grid"]) == (1, 35, 6, 6, 252)
+    assert p["workspace_bytes"] == 8 * 35 * 576 * 1036 + 8 * 4
     # the stride never exceeds ceil(tiles / 4) of the longest allowed sequence
     p = B.plan(2, 9, 8, 300)                   # 10 tiles -> at most 3 splits each, 6 in all
     assert (p["balanced"], p["nsplit"], p["grid"]) == (1, 3, 6)
@@ -147,7 +161,11 @@ def test_plan_balanced_splits(L):
     assert B.plan(8, 9, 64, 26681, nsplit=3)["balanced"] == 0
     assert B.plan(1, 9, 8, 65545)["balanced"] == 0
     assert B.plan(65, 1, 8, 4096)["balanced"] == 0
-    assert B.plan(30, 9, 64, 4096)["balanced"] == 0   # 28 units < 30 sequences
+    assert B.plan(60, 9, 64, 4096)["balanced"] == 0   # 42 units < 60 sequences
+    # 30 sequences: 8 groups of 5 blocks fit one pass (240 workgroups), and
+    # the 32 units they leave cover the batch
+    p = B.plan(30, 9, 64, 4096)
+    assert (p["balanced"], p["row_blocks"], p["row_groups"], p["nsplit"]) == (1, 5, 8, 3)
     assert B.plan(2, 9, 8, 100)["balanced"] == 0      # 4 tiles: one split each anyway
 
 
@@ -155,7 +173,7 @@ def test_plan_shapes_fp8_topk(L):
     fp8 = dict(kv_dtype=B.MLA_KV_FP8_E4M3, mask="topk", topk=2048)
     p = B.plan(32, 1, 64, 65536, nsplit=8, **fp8)     # one query per sequence, 64 heads = 4 blocks
     assert (p["kernel"], p["row_blocks"], p["row_groups"], p["grid"]) == (1, 4, 1, 8 * 32)
-    assert p["workspace_bytes"] == 32 * 8 * 64 * 1036
+    assert p["workspace_bytes"] == 32 * 8 * 64 * 1036 + 32 * 4
     p = B.plan(2, 3, 80, 5000, nsplit=2, **fp8)       # 5 blocks -> groups of at most 4; grid over (seq, query)
     assert (p["row_blocks"], p["row_groups"], p["grid"]) == (4, 2, 2 * 2 * 2 * 3)
     p = B.plan(1, 1, 8, 100, nsplit=1, **fp8)
@@ -168,7 +186,7 @@ def test_plan_shapes_fp8_topk(L):
 
 def test_workspace_bytes(L):
     assert B.workspace_bytes(1, 9, 8, 1) == 0
-    assert B.workspace_bytes(3, 9, 8, 16) == 3 * 16 * 72 * 1036
+    assert B.workspace_bytes(3, 9, 8, 16) == 3 * 16 * 72 * 1036 + 3 * 4
 
 
 def test_host_tree_mask_bit_exact_vs_oracle(L):
