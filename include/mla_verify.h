@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 2
+#define MLA_VERIFY_ABI_VERSION 3
 
 /* Status codes. */
 #define MLA_OK 0
@@ -138,6 +138,9 @@ typedef struct mla_plan_t {
   int row_blocks;        /* 16-row query blocks per workgroup */
   int balanced;          /* 1: split counts follow the sequence lengths (see
                             mla_verify_attn); nsplit is then their upper bound */
+  int l2_prefetch;       /* 1: the bf16 split kernel pulls cache lines into L2
+                            four tiles ahead of its gathers (splits of at
+                            least 24 tiles of 32 positions) */
 } mla_plan_t;
 
 /*

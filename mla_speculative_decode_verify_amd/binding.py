@@ -64,7 +64,7 @@ class MlaMask(ctypes.Structure):
 class MlaPlan(ctypes.Structure):
     _fields_ = [("nsplit", ctypes.c_int), ("waves_per_group", ctypes.c_int), ("row_groups", ctypes.c_int),
                 ("grid", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int),
-                ("row_blocks", ctypes.c_int), ("balanced", ctypes.c_int)]
+                ("row_blocks", ctypes.c_int), ("balanced", ctypes.c_int), ("l2_prefetch", ctypes.c_int)]
 
 
 _lib = None

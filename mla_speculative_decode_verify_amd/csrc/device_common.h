@@ -82,6 +82,14 @@ __device__ __forceinline__ void lds_dma_b128(const void* src, uint32_t lds_addr)
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
 }
 
+// Global-to-LDS load of 4 bytes per lane (global_load_lds_dword): lane i's
+// word lands at LDS byte address lds_addr + 4 i. Counted and drained by the
+// caller like lds_dma_b128; used to pull cache lines into L2 ahead of the
+// 16-byte gathers that will read them (the landed words are never read).
+__device__ __forceinline__ void lds_dma_b32(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
 // 32-bit LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;

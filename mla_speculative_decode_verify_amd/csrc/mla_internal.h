@@ -42,6 +42,8 @@ struct Args {
   int balance_units;        // > 0: per-sequence split counts follow the lengths
                             // (balanced_split), with at most this many splits in all
   int row_groups;           // workgroups along the row axis (set at launch)
+  int l2_prefetch;          // bf16 split kernel: pull cache lines into L2 a few tiles ahead of
+                            // the gathers (long splits only; set by the plan)
   int mask_kind;
   int topk;
   float scale_log2;         // sm_scale * log2(e)

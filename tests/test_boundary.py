@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 12, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/mla_verify.h but not exported"
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
 
 
 def test_status_strings(L):
@@ -125,6 +125,14 @@ def test_choose_nsplit_rules(L):
     # instead of 1.86, 3.3 us more fixed cost)
     p = B.plan(1, 9, 64, 65545)
     assert (p["nsplit"], p["row_blocks"], p["row_groups"], p["grid"]) == (42, 6, 6, 252)
+    # L2 prefetch ahead of the gathers from 24 tiles per split: 49 here, 17
+    # at 16k, 9 for one H=8 rank at 64k
+    assert p["l2_prefetch"] == 1
+    assert B.plan(1, 9, 64, 16393)["l2_prefetch"] == 0
+    assert B.plan(1, 9, 8, 65545)["l2_prefetch"] == 0
+    assert B.plan(1, 9, 8, 65545, nsplit=64)["l2_prefetch"] == 1   # 33 tiles each
+    assert B.plan(1, 9, 8, 65545, nsplit=86)["l2_prefetch"] == 1   # 2049 tiles: 24 in the longest
+    assert B.plan(1, 9, 8, 65545, nsplit=90)["l2_prefetch"] == 0   # 23
     assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 4          # 4 tiles: 7.4 us alone, 1.9 + 4.1 split
     assert B.choose_nsplit(1, 9, 8, 32, num_cus=256) == 1
     assert B.choose_nsplit(32, 1, 64, 2048, kv_dtype=B.MLA_KV_FP8_E4M3, num_cus=256) == 8
@@ -153,6 +161,7 @@ def test_plan_balanced_splits(L):
     p = B.plan(8, 9, 64, 26681)
     assert (p["balanced"], p["nsplit"], p["row_groups"], p["row_blocks"], p["grid"]) == (1, 35, 6, 6, 252)
     assert p["workspace_bytes"] == 8 * 35 * 576 * 1036 + 8 * 4
+    assert p["l2_prefetch"] == 1                # 834 tiles over a stride of 35
     # the stride never exceeds ceil(tiles / 4) of the longest allowed sequence
     p = B.plan(2, 9, 8, 300)                   # 10 tiles -> at most 3 splits each, 6 in all
     assert (p["balanced"], p["nsplit"], p["grid"]) == (1, 3, 6)
