@@ -41,6 +41,8 @@ def test_c1_small_verify():
 
 
 def test_c2_full_heads():
+    # 8, 16 and the library's 26 splits run 9 row groups of 4 blocks; 32 and
+    # 64 run 8 groups of 5, the last with one live block
     _check(I.workload("c2"), [8, 16, 32, 64, 0])
 
 
@@ -55,6 +57,9 @@ def test_c3_64k_random_slots():
 def test_h64_prefix_64k_sampled_heads():
     # the pages' largest sweep point: q_len 9, H=64, prefix 65536 (every head
     # computed on the GPU; the oracle checks a sample of them)
+    # the library's plan: 6 row groups of 6 blocks, 42 splits of 49 tiles
+    # with the L2 prefetch; 16 splits: 9 groups of 4, 129 tiles over three
+    # 2048-position chunks, prefetching across them
     w = I.workload("sweep_65536")
     _check(w, [0, 16], heads=[0, 31, 63])
 
@@ -71,7 +76,7 @@ def test_c4_tree_ragged_sampled_heads():
     (64, 2, [70], "causal"),          # maximum q_len
     (9, 16, [1000, 37], "none"),      # no mask, ragged
     (7, 20, [300], "tree"),           # 140 rows -> several row groups
-    (2, 128, [513, 64], "causal"),    # the largest head count: 256 rows in row groups of 80
+    (2, 128, [513, 64], "causal"),    # the largest head count: 256 rows in several row groups
     (9, 8, [int(x) for x in np.random.default_rng(3).integers(0, 700, size=40)], "tree"),  # 40 ragged sequences
 ])
 def test_edge_shapes(q_len, heads, prefixes, mask):
@@ -83,7 +88,7 @@ def test_edge_shapes(q_len, heads, prefixes, mask):
 @pytest.mark.parametrize("heads,prefixes,mask", [
     (8, [0, 40000], "causal"),        # one sequence takes nearly all splits, the other one
     (8, [int(x) for x in np.random.default_rng(7).integers(0, 3000, size=64)], "tree"),  # 64: one per lane
-    (64, [5000, 300, 12000], "tree"),  # 9 row groups: 28 splits shared by 3 sequences
+    (64, [5000, 300, 12000], "tree"),  # 6 row groups of 6 blocks: 42 splits shared by 3 sequences
 ])
 def test_length_following_splits(heads, prefixes, mask):
     # library-chosen splits on a ragged batch: the split counts follow the
