@@ -245,3 +245,32 @@ def test_topk_workspace_bytes(L):
     # per row: 8 parts of 8192 positions -> histograms, candidate pairs, row and part counters
     assert B.topk_workspace_bytes(32, 1, 65536) == 32 * (8 * 2048 * 4 + 8 * 8192 * 8 + 16 + 8 * 12)
     assert B.topk_workspace_bytes(0, 1, 64) == 0
+
+
+def test_plan_invariants_over_shapes(L):
+    # Library-chosen plans over a grid of bf16 shapes: at most six blocks per
+    # workgroup and enough groups for every row, a one-pass grid whenever a
+    # split count of 1 already fits the CUs, no more splits than tiles, a
+    # workspace that matches the split count, and L2 prefetch exactly when
+    # the longest split holds 24 tiles or more.
+    for batch in (1, 3, 8):
+        for q_len, heads in ((1, 8), (9, 8), (9, 16), (9, 64), (4, 128), (64, 2)):
+            for n in (9, 300, 4105, 16393, 65545):
+                if n < q_len:
+                    continue
+                p = B.plan(batch, q_len, heads, n)
+                rows = q_len * heads
+                blocks = (rows + 15) // 16
+                assert 1 <= p["row_blocks"] <= 6
+                assert p["row_groups"] * p["row_blocks"] >= blocks
+                assert (p["row_groups"] - 1) * p["row_blocks"] < blocks
+                assert p["waves_per_group"] == 2 * p["row_blocks"]
+                tiles = -(-n // 32)
+                if p["balanced"]:
+                    assert p["grid"] <= 256
+                else:
+                    assert 1 <= p["nsplit"] <= tiles
+                    if batch * p["row_groups"] <= 256:
+                        assert p["grid"] <= 256
+                    assert (p["workspace_bytes"] == 0) == (p["nsplit"] == 1)
+                    assert p["l2_prefetch"] == int(-(-tiles // p["nsplit"]) >= 24)
