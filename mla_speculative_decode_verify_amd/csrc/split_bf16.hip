@@ -486,9 +486,10 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const float ltr = group4_sum(lr);
   const float inv = ltr > 0.f ? 1.f / ltr : 0.f;
   const float lse_v = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
-  // the tile ring is free now: 8 KiB of it per wavefront stages the stores
+  // the tile ring is free now: kStageHalves of it per wavefront stage the stores
+  static_assert(NW * kStageHalves * 2 <= (int)sizeof(kv), "staging areas fit the tile ring");
   store_block_half(a, o, inv, lse_v, b, split, row0, min(16, R - row0), half, g, half == 0 && g == 0,
-                   reinterpret_cast<_Float16*>(kv) + wave * 4096);
+                   reinterpret_cast<_Float16*>(kv) + wave * kStageHalves);
 }
 
 template <int NB, bool kPf>

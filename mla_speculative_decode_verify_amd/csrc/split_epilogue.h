@@ -18,15 +18,22 @@ namespace mla {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
+// Staging rows are padded by 16 halves (32 bytes): with a bare 512-byte
+// stride the 16 rows of one 8-byte write instruction all hit the same LDS
+// banks (a 16-way conflict on every staging write); with a stride of 136
+// words each group of rows covers every bank once.
+constexpr int kStageRow = 256 + 16;              // halves per staged row
+constexpr int kStageHalves = 16 * kStageRow;     // one wavefront's staging area (8.5 KiB)
+
 // Lane (g, li) holds o[d][r] (d < 16) = unnormalised output column
 // 256 half + 16 d + 4 g + r of block row li; `inv` normalises it.
 // All 64 lanes must call this (it reduces across lanes). The block's rows
 // are r_first .. r_first + n_valid - 1 within the sequence (n_valid <= 16),
 // so lane li's row exists iff li < n_valid.
-// `stage` is 8 KiB of LDS owned by this wavefront alone (free after the
-// tile loop): fp16 partials are transposed through it so that every store
-// instruction writes two whole 512-byte row halves instead of 32-byte
-// pieces of 16 rows.
+// `stage` is kStageHalves halves of LDS owned by this wavefront alone (free
+// after the tile loop): fp16 partials are transposed through it so that
+// every store instruction writes two whole 512-byte row halves instead of
+// 32-byte pieces of 16 rows.
 __device__ __forceinline__ void store_block_half(const Args& a, const f32x4* o, float inv, float lse_v,
                                                  int b, int split, int r_first, int n_valid, int half, int g,
                                                  bool write_lse, _Float16* stage) {
@@ -53,11 +60,11 @@ __device__ __forceinline__ void store_block_half(const Args& a, const f32x4* o, 
   const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127;
   const int e = min(max(ex - 14, -126), 113);
   const float down = __builtin_amdgcn_ldexpf(inv, -e);
-  // stage[row li][256 columns] in fp16, then 16-byte pieces row-major
+  // stage[row li][256 columns (row stride kStageRow)] in fp16, then 16-byte pieces row-major
 #pragma unroll
   for (int d = 0; d < kBlocks; ++d) {
     const f32x4 v = o[d] * down;
-    *reinterpret_cast<f16x4*>(stage + li * 256 + 16 * d + 4 * g) = __builtin_convertvector(v, f16x4);
+    *reinterpret_cast<f16x4*>(stage + li * kStageRow + 16 * d + 4 * g) = __builtin_convertvector(v, f16x4);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
@@ -65,7 +72,7 @@ __device__ __forceinline__ void store_block_half(const Args& a, const f32x4* o, 
   for (int i = 0; i < 8; ++i) {
     const int q = lane + 64 * i;       // 16-byte piece: row q / 32, column piece q % 32
     const int rr = q >> 5, cp = q & 31;
-    const f32x4 piece = *reinterpret_cast<const f32x4*>(stage + rr * 256 + 8 * cp);
+    const f32x4 piece = *reinterpret_cast<const f32x4*>(stage + rr * kStageRow + 8 * cp);
     if (rr < n_valid) {
       const size_t pr = ((size_t)b * S + split) * R + r_first + rr;
       // streaming store: the partials are read once, by the merge kernel

@@ -371,8 +371,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
   const float inv = ltr > 0.f ? 1.f / ltr : 0.f;
   const float lse_v = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
   // the tile buffers are free now: 8 KiB of them per wavefront stage the stores
+  static_assert(NW * kStageHalves * 2 <= (int)sizeof(kv), "staging areas fit the tile buffers");
   store_block_half(a, o, inv, lse_v, b, split, qi * H + row0, min(16, H - row0), half, g, half == 0 && g == 0,
-                   reinterpret_cast<_Float16*>(kv) + wave * 4096);
+                   reinterpret_cast<_Float16*>(kv) + wave * kStageHalves);
 }
 
 template <int NB>
