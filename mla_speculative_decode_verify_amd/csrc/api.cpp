@@ -140,9 +140,10 @@ double bf16_cost_us(int nb, long wgs_per_split, long tiles, long s, long rows_to
   return t;
 }
 
-// Best split count for `nb` blocks in `groups` workgroups per key set: one
-// workgroup per CU at most (a split workgroup fills a CU), so the grid runs
-// in a single pass; the cheapest count wins, the fewest on ties.
+// Best split count for `nb` blocks per workgroup and `wgs_per_split`
+// workgroups per split (key sets times row groups): one workgroup per CU at
+// most (a split workgroup fills a CU), so the grid runs in a single pass;
+// the cheapest count wins, the fewest on ties.
 long bf16_best_split(int nb, long wgs_per_split, long tiles, long rows_total, int num_cus, double* cost) {
   const long one_pass = std::max<long>(1, num_cus / wgs_per_split);
   long s = 1;
