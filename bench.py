@@ -281,8 +281,17 @@ def main():
         "algorithmic": {"bytes": cnt["bytes"], "flops": cnt["flops"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "gpu": gpu_info(),
     }
     print(json.dumps(line), flush=True)
+
+
+def gpu_info():
+    """Device name, architecture and CU count as the runtime reports them."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count}
 
 
 def bench_append(args, w):
