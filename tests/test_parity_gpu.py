@@ -187,3 +187,42 @@ def test_partials_keep_value_range(factor):
         torch.cuda.synchronize()
         compare(out / factor, lse, ref_out / factor, ref_lse, f"range {factor} nsplit={ns}")
     assert B.device_error() == 0
+
+
+def test_mixed_plans_share_the_workspace():
+    # Calls with different plans run back to back on one stream and share the
+    # library's workspace: uniform splits with one 5-block group (H=8),
+    # length-following splits with 6-block groups and the L2 prefetch (ragged
+    # tree batch, H=64), 8 groups of 5 blocks (H=64), and the fp8 sparse path.
+    # Each result must equal, bit for bit, the same call made first on its
+    # own, whatever ran between (stale split counts or partials would show).
+    import numpy as np
+
+    shapes = [
+        I.make_verify("mix_h8", batch=1, q_len=9, heads=8, prefixes=[9000], seed=61, layout="random"),
+        I.make_verify("mix_ragged", batch=3, q_len=9, heads=64, prefixes=[30000, 700, 12000], seed=62,
+                      layout="random", mask="tree"),
+        I.make_verify("mix_h64", batch=1, q_len=9, heads=64, prefixes=[16000], seed=63, layout="contiguous"),
+        I.workload("c5"),
+    ]
+    devs = [DeviceInputs(w) for w in shapes]
+    first = []
+    for d in devs:
+        o, l = d.run()
+        torch.cuda.synchronize()
+        first.append((o.clone(), l.clone()))
+    plans = [B.plan(w.batch, w.q_len, w.heads, w.slot_stride, mask=w.mask) for w in shapes[:3]]
+    assert plans[0]["row_blocks"] == 5 and plans[0]["balanced"] == 0
+    assert plans[1]["balanced"] == 1 and plans[1]["row_blocks"] == 6 and plans[1]["l2_prefetch"] == 1
+    assert plans[2]["row_blocks"] == 5 and plans[2]["row_groups"] == 8
+    order = [1, 0, 3, 2, 1, 3, 0, 2, 1]
+    for k in order:
+        _log(f"[mixed] {shapes[k].name}")
+        o, l = devs[k].run()
+        torch.cuda.synchronize()
+        assert torch.equal(o, first[k][0]) and torch.equal(l, first[k][1]), shapes[k].name
+    # and the first of them still matches the oracle
+    ref_out, ref_lse = oracle(shapes[0])
+    compare(first[0][0], first[0][1], ref_out, ref_lse, shapes[0].name)
+    assert B.device_error() == 0
+    assert np.isfinite(first[1][1].cpu().numpy()).all()
