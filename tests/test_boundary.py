@@ -268,6 +268,9 @@ def test_plan_invariants_over_shapes(L):
                 tiles = -(-n // 32)
                 if p["balanced"]:
                     assert p["grid"] <= 256
+                    # the stride bounds every sequence's count, so the longest
+                    # sequence's splits hold at least ceil(tiles / stride) tiles
+                    assert p["l2_prefetch"] == int(-(-tiles // p["nsplit"]) >= 24)
                 else:
                     assert 1 <= p["nsplit"] <= tiles
                     if batch * p["row_groups"] <= 256:
