@@ -169,13 +169,38 @@ def cpu_baseline(w, reps=3):
 
         def run():
             O.verify_attention(w.q_bits, w.pool_bits, w.slot_table, w.seq_lens, anc, w.sm_scale)
-    ts = []
-    for _ in range(reps):
-        t = time.perf_counter()
-        run()
-        ts.append(time.perf_counter() - t)
-    return dict(value=statistics.median(ts) * 1e6, unit="us/call", cores=int(threads), kind="oracle",
-                sample=f"the full {w.name} call (all {w.batch * w.q_len * w.heads} query rows), median of {reps}")
+    def timed():
+        ts = []
+        for _ in range(reps):
+            t = time.perf_counter()
+            run()
+            ts.append(time.perf_counter() - t)
+        return statistics.median(ts) * 1e6
+
+    out = dict(value=timed(), unit="us/call", cores=int(threads), kind="oracle",
+               sample=f"the full {w.name} call (all {w.batch * w.q_len * w.heads} query rows), median of {reps}",
+               cpu_model=cpu_model(), os_cpu_count=os.cpu_count())
+    if w.name in ("c1", "c2", "c3_16k", "c3_64k"):
+        # the same oracle with its BLAS limited to one thread
+        try:
+            from threadpoolctl import threadpool_limits
+
+            with threadpool_limits(limits=1):
+                out["one_thread_us"] = timed()
+        except Exception:  # pragma: no cover
+            out["one_thread_us"] = None
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -249,7 +274,9 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         cpu = cpu_baseline(w)
-        log(f"[bench] oracle {cpu['value']:.0f} us/call on {cpu['cores']} threads")
+        cpu["gpu_speedup"] = round(cpu["value"] / cold, 1)
+        log(f"[bench] oracle {cpu['value']:.0f} us/call on {cpu['cores']} threads "
+            f"(one thread: {cpu.get('one_thread_us')}), {cpu['gpu_speedup']}x the GPU call")
     line = {
         "metric": METRIC,
         "value": round(cold, 3),
