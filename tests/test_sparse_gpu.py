@@ -142,6 +142,33 @@ def test_verify_bad_slot_is_masked_and_flagged():
         assert B.device_error() == B.MLA_DEVERR_SLOT_RANGE
 
 
+def test_verify_bad_slots_in_long_prefetching_splits():
+    # Long splits (about 79 tiles of 32 positions, so two staged chunks each)
+    # take the L2 prefetch, which reads the staged row addresses four tiles
+    # ahead: invalid slots are staged as the zero row there too, so they are
+    # dropped like masked keys wherever they fall (first tile, chunk edge,
+    # prefetch distance) and raise the slot-range flag.
+    w = I.make_verify("badslot_long", batch=1, q_len=9, heads=8, prefixes=[20000], seed=76, layout="random")
+    assert B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=8)["l2_prefetch"] == 1
+    B.device_error()
+    bad = [0, 31, 32, 2047, 2048, 2600, 2629, 5101, 19990]
+    slots = w.slot_table.copy()
+    for k, pos in enumerate(bad):
+        slots[0, pos] = w.pool_rows + 7 + k if k % 2 == 0 else -1 - k
+    keep = np.setdiff1d(np.arange(int(w.seq_lens[0])), bad)
+    ref_slots = np.zeros_like(w.slot_table)
+    ref_slots[0, :keep.size] = w.slot_table[0, keep]
+    ref_w = I.VerifyInputs(**{**w.__dict__, "slot_table": ref_slots,
+                              "seq_lens": np.array([keep.size], dtype=np.int32)})
+    ref_out, ref_lse = oracle(ref_w)
+    d = DeviceInputs(I.VerifyInputs(**{**w.__dict__, "slot_table": slots}))
+    for ns in (8, 3):
+        out, lse = d.run(nsplit=ns)
+        torch.cuda.synchronize()
+        compare(out, lse, ref_out, ref_lse, f"badslot_long nsplit={ns}")
+        assert B.device_error() == B.MLA_DEVERR_SLOT_RANGE
+
+
 @pytest.mark.parametrize("nsplit", [3, 8, 40, 0])
 def test_sparse_stages_equal_full_call(nsplit):
     # Split and merge entry points called in turn equal the full call bit
