@@ -129,9 +129,6 @@ constexpr double kFixedUs[7] = {0.0, 8.1, 8.1, 8.1, 8.1, 8.1, 11.4};
 constexpr double kPartUsPerByte = 0.49e-6;
 constexpr double kMergeUs = 4.0;
 constexpr int kMaxBlocks = 6;
-// Tiles per split from which the bf16 split kernel prefetches cache lines
-// into L2 (the kernel's own per-split threshold is the same).
-constexpr int kPfMinTiles = 24;
 
 double bf16_cost_us(int nb, long wgs_per_split, long tiles, long s, long rows_total, int num_cus) {
   const long passes = (wgs_per_split * s + num_cus - 1) / num_cus;
@@ -301,7 +298,7 @@ int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsp
   // longest split of a uniform count, or of the stride of length-following
   // counts (a lower bound of the longest sequence's tiles per split).
   const long max_tiles = ((long)maxlen + 31) / 32;
-  c->a.l2_prefetch = c->kernel == 0 && (max_tiles + s - 1) / s >= kPfMinTiles ? 1 : 0;
+  c->a.l2_prefetch = c->kernel == 0 && (max_tiles + s - 1) / s >= mla::kPfMinTiles ? 1 : 0;
   return MLA_OK;
 }
 

@@ -11,6 +11,10 @@ namespace mla {
 constexpr int kDk = 576;    // absorbed query / key width (512 latent ++ 64 rope)
 constexpr int kDv = 512;    // value width: the latent part of the same row
 constexpr int kDrope = 64;
+// Splits of at least this many 32-position tiles take the bf16 split
+// kernel's L2 prefetch (the plan picks the instantiation; the kernel checks
+// each split's own length).
+constexpr int kPfMinTiles = 24;
 
 // Everything a kernel needs, with pointers already validated by the host.
 struct Args {

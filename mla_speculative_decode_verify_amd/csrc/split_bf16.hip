@@ -83,7 +83,7 @@ constexpr int kPfAhead = MLA_PF_AHEAD;
 // starts at once, so their first tiles already arrive in one burst that
 // saturates HBM, and extra requests only delay them (measured: 9-tile
 // splits slower by 3 us, 100-tile splits of random slots faster by 25%).
-constexpr int kPfMinKeys = 24 * kTile;
+constexpr int kPfMinKeys = kPfMinTiles * kTile;
 constexpr int kRowLines = kDk * 2 / 128;                  // 128-byte lines per cache row (9)
 constexpr int kPfOps = (kTile * kRowLines + 63) / 64;     // wave loads per prefetched tile (5)
 
