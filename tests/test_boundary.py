@@ -277,3 +277,5 @@ def test_plan_invariants_over_shapes(L):
                         assert p["grid"] <= 256
                     assert (p["workspace_bytes"] == 0) == (p["nsplit"] == 1)
                     assert p["l2_prefetch"] == int(-(-tiles // p["nsplit"]) >= 24)
+                    # the exported split-count rule is the plan's
+                    assert B.choose_nsplit(batch, q_len, heads, n, num_cus=256) == p["nsplit"]
