@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--nsplit", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough for > 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", default="c3_16k,sweep_16384,sweep_65536",
+                    help="comma-separated workloads also timed (cold, warm, graph replay) and reported in the "
+                         "same JSON line under 'secondary'; empty to skip")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--op", default="verify", choices=["verify", "append", "topk", "absorb"],
                     help="append: time the draft-KV append (mla_append_kv) for the workload's shape instead; "
                          "topk: time the top-k selection (mla_topk_select) feeding a sparse workload; "
@@ -148,6 +152,98 @@ def time_calls(calls, steps, warmup, rotate=True):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
+def time_graph(rot, steps, warmup):
+    """Average µs per call when the calls (one per rotation copy, in order) are captured into one HIP
+    graph and the graph is replayed: no host launch gaps between the kernels. Events on the replay stream."""
+    import torch
+
+    from mla_speculative_decode_verify_amd import binding as B
+
+    calls = rot.calls["both"]
+    s = torch.cuda.Stream()
+    B.reserve_workspace(rot.plan["workspace_bytes"], stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    reps = max(1, steps // len(calls))
+    with torch.cuda.stream(s):
+        for _ in range(max(1, warmup // len(calls))):
+            g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+    del g
+    torch.cuda.synchronize()
+    B.release_workspace(stream=s)
+    return us
+
+
+def measure(w, args, nsplit, copies=0, graph=True):
+    """Cold / warm / split-kernel / merge-kernel (and graph-replay) µs per call of workload `w`."""
+    from mla_speculative_decode_verify_amd import roofline as RL
+
+    if w.kind == "sparse":
+        cnt = RL.sparse_counts(w.batch, w.q_len, w.heads, w.meta["topk"])
+        read_bytes = w.batch * w.q_len * w.meta["topk"] * 652
+    else:
+        cnt = RL.verify_counts(w.q_len, w.heads, w.seq_lens.tolist(), mask=w.mask,
+                               parents=None if w.parents is None else w.parents.tolist())
+        read_bytes = w.seq_lens.astype("int64").sum() * 1152
+    copies = copies or max(2, int(-(-(1 << 30) // int(read_bytes))) + 1)
+    log(f"[bench] {describe(w)}; copies {copies}")
+    rot = Rotation(w, copies, nsplit)
+    plan = rot.plan
+    log(f"[bench] plan {plan}")
+    r = dict(cnt=cnt, copies=copies, plan=plan)
+    r["cold"] = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=True)
+    r["warm"] = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=False)
+    r["split"] = time_calls(rot.calls["split"], args.steps, args.warmup, rotate=True)
+    r["combine"] = (time_calls(rot.calls["combine"], args.steps, args.warmup, rotate=True)
+                    if plan["nsplit"] > 1 else 0.0)
+    r["graph"] = time_graph(rot, args.steps, args.warmup) if graph else None
+    log(f"[bench] cold {r['cold']:.2f} us/call, warm {r['warm']:.2f}, split kernel {r['split']:.2f}, "
+        f"combine {r['combine']:.2f}, graph replay {r['graph']}")
+    del rot
+    return r
+
+
+def roofline_entry(w, r):
+    """Roofline object: achieved and frac for the whole call (cold µs, as `value`), and the same for the
+    split kernel alone (the dominant kernel, whose duration the rocprofv3 summaries give)."""
+    from mla_speculative_decode_verify_amd import roofline as RL
+
+    cnt = r["cnt"]
+    rf = RL.roofline_us(cnt["flops"], cnt["bytes"])
+    hbm = rf["bound"] == "hbm"
+    peak = RL.PEAK_HBM_GBPS if hbm else RL.PEAK_BF16_TFLOPS
+
+    def ach(us):
+        return cnt["bytes"] / (us * 1e-6) / 1e9 if hbm else cnt["flops"] / (us * 1e-6) / 1e12
+
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        try:
+            tr = json.load(open(PROFILE_TRAFFIC))
+            key = f"{w.name}/nsplit{r['plan']['nsplit']}"
+            if key in tr and tr[key].get("kernel_source_hash") == kernel_hash(w.kind):
+                traffic = tr[key]["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    return dict(bound=rf["bound"], achieved=round(ach(r["cold"]), 2), peak=peak,
+                unit="GB/s" if hbm else "TFLOP/s", frac=round(ach(r["cold"]) / peak, 4), traffic=traffic,
+                scope="whole call (split + merge kernels, cold)",
+                split_kernel_us=round(r["split"], 3), split_kernel_achieved=round(ach(r["split"]), 2),
+                split_kernel_frac=round(ach(r["split"]) / peak, 4), roofline_us=round(rf["us"], 3))
+
+
 def cpu_baseline(w, reps=3):
     import numpy as np
 
@@ -228,40 +324,11 @@ def main():
     if args.op == "absorb":
         bench_absorb(args, w)
         return
-    if w.kind == "sparse":
-        cnt = RL.sparse_counts(w.batch, w.q_len, w.heads, w.meta["topk"])
-        read_bytes = w.batch * w.q_len * w.meta["topk"] * 652
-    else:
-        cnt = RL.verify_counts(w.q_len, w.heads, w.seq_lens.tolist(), mask=w.mask,
-                               parents=None if w.parents is None else w.parents.tolist())
-        read_bytes = w.seq_lens.astype("int64").sum() * 1152
-    copies = args.copies or max(2, int(-(-(1 << 30) // int(read_bytes))) + 1)
-    log(f"[bench] {describe(w)}; copies {copies}")
-    rot = Rotation(w, copies, args.nsplit)
-    plan = rot.plan
-    log(f"[bench] plan {plan}")
-
-    cold = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=True)
-    warm = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=False)
-    split_us = time_calls(rot.calls["split"], args.steps, args.warmup, rotate=True)
-    comb_us = time_calls(rot.calls["combine"], args.steps, args.warmup, rotate=True) if plan["nsplit"] > 1 else 0.0
-    log(f"[bench] cold {cold:.2f} us/call, warm {warm:.2f}, split kernel {split_us:.2f}, combine {comb_us:.2f}")
-
+    r = measure(w, args, args.nsplit, args.copies, graph=not args.no_graph)
+    cnt, plan, cold, warm, copies = r["cnt"], r["plan"], r["cold"], r["warm"], r["copies"]
+    split_us, comb_us = r["split"], r["combine"]
     rf = RL.roofline_us(cnt["flops"], cnt["bytes"])
-    achieved_gbps = cnt["bytes"] / (split_us * 1e-6) / 1e9
-    peak = RL.PEAK_HBM_GBPS if rf["bound"] == "hbm" else RL.PEAK_BF16_TFLOPS
-    ach = achieved_gbps if rf["bound"] == "hbm" else cnt["flops"] / (split_us * 1e-6) / 1e12
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
-        try:
-            tr = json.load(open(PROFILE_TRAFFIC))
-            key = f"{w.name}/nsplit{plan['nsplit']}"
-            if key in tr and tr[key].get("kernel_source_hash") == kernel_hash(w.kind):
-                traffic = tr[key]["bytes_per_launch"]
-        except Exception:
-            traffic = None
-    roof = dict(bound=rf["bound"], achieved=round(ach, 2), peak=peak, unit="GB/s" if rf["bound"] == "hbm" else "TFLOP/s",
-                frac=round(ach / peak, 4), traffic=traffic)
+    roof = roofline_entry(w, r)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -277,6 +344,24 @@ def main():
         cpu["gpu_speedup"] = round(cpu["value"] / cold, 1)
         log(f"[bench] oracle {cpu['value']:.0f} us/call on {cpu['cores']} threads "
             f"(one thread: {cpu.get('one_thread_us')}), {cpu['gpu_speedup']}x the GPU call")
+    secondary = {}
+    names = [n for n in args.secondary.split(",") if n and n != w.name] if args.op == "verify" else []
+    for name in names:
+        torch.cuda.empty_cache()
+        w2 = I.workload(name)
+        r2 = measure(w2, args, 0, 0, graph=not args.no_graph)
+        secondary[name] = {
+            "workload": describe(w2), "us_per_call": round(r2["cold"], 3), "warm_us": round(r2["warm"], 3),
+            "graph_us": None if r2["graph"] is None else round(r2["graph"], 3),
+            "kernels_us": {"split": round(r2["split"], 3), "combine": round(r2["combine"], 3)},
+            "nsplit": r2["plan"]["nsplit"], "row_blocks": r2["plan"]["row_blocks"],
+            "row_groups": r2["plan"]["row_groups"],
+            "algorithmic": {"bytes": r2["cnt"]["bytes"], "flops": r2["cnt"]["flops"]},
+            "achieved_TBps": round(r2["cnt"]["bytes"] / (r2["cold"] * 1e-6) / 1e12, 4),
+            "achieved_TFLOPs": round(r2["cnt"]["flops"] / (r2["cold"] * 1e-6) / 1e12, 3),
+            "roofline": roofline_entry(w2, r2),
+        }
+        del w2, r2
     line = {
         "metric": METRIC,
         "value": round(cold, 3),
@@ -300,6 +385,7 @@ def main():
                    "waves_per_group": plan["waves_per_group"],
                    "row_groups": plan["row_groups"], "grid": plan["grid"], "cold_copies": copies},
         "warm_us": round(warm, 3),
+        "graph_us": None if r["graph"] is None else round(r["graph"], 3),
         "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3)},
         "achieved_TBps": round(cnt["bytes"] / (cold * 1e-6) / 1e12, 4),
         "achieved_TFLOPs": round(cnt["flops"] / (cold * 1e-6) / 1e12, 3),
@@ -308,6 +394,7 @@ def main():
         "algorithmic": {"bytes": cnt["bytes"], "flops": cnt["flops"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "secondary": secondary,
         "gpu": gpu_info(),
     }
     print(json.dumps(line), flush=True)

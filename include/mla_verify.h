@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 3
+#define MLA_VERIFY_ABI_VERSION 4
 
 /* Status codes. */
 #define MLA_OK 0
@@ -164,11 +164,15 @@ typedef struct mla_plan_t {
  *               sequence of t tiles then gets ceil(t / T) splits, at most
  *               ceil(t / 4) and at least 1, for the smallest T that keeps
  *               the total within the grid. Capped at MLA_MAX_NSPLIT.
- * When nsplit > 1 the call uses the library's workspace for (device,
- * stream): it grows on demand (synchronising `stream` first), or returns
- * MLA_ERR_WORKSPACE if the stream is capturing and the reserve is too small.
- * Calls on the same stream are ordered; calls on different streams have
- * separate workspaces.
+ * When nsplit > 1 the call keeps its split partials in the library's
+ * workspace for (device, stream): it grows on demand (synchronising `stream`
+ * first), or returns MLA_ERR_WORKSPACE if the stream is capturing and the
+ * reserve is too small. Calls on the same stream are ordered; calls on
+ * different streams have separate workspaces. A graph captured on a stream
+ * keeps using that stream's workspace when it is replayed, whatever stream
+ * it is replayed on: the caller must order replays against eager calls made
+ * on the capture stream (e.g. replay on that stream), or they race on the
+ * partials. See mla_reserve_workspace / mla_release_workspace.
  */
 int mla_verify_attn(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table,
                     const int32_t* seq_lens, const mla_mask_t* mask_desc, float* out, float* lse,
@@ -214,13 +218,33 @@ int mla_choose_nsplit(int batch, int q_len, int heads, int max_seq_len, int kv_d
 /* Bytes of split partials one call needs: batch * nsplit * q_len * heads *
  * (512 * 2 + 12) (fp16 partial output, its two power-of-two scales and the
  * fp32 LSE per split and row) plus batch * 4 (each sequence's split count
- * when the counts follow the lengths), or 0 for nsplit <= 1. */
+ * when the counts follow the lengths), or 0 for nsplit <= 1. For a ragged
+ * batch whose split counts follow the lengths, nsplit here must be the
+ * partials' stride, which can exceed mla_choose_nsplit's uniform count:
+ * the size to reserve for a given call is mla_plan(...).workspace_bytes.
+ * ("How One Environment Variable Unlocked 3x Throughput", section "The
+ * Occupancy Revelation": the partial buffers grow with NSPLIT and are
+ * sized ahead of graph capture; section "Assumptions Underlying the
+ * Reasoning", item 5: the kernel runs inside captured graphs and must not
+ * allocate there.) */
 size_t mla_workspace_bytes(int batch, int q_len, int heads, int nsplit);
 
-/* Make the workspace of (current device, stream) at least `bytes` long and
- * allocate the device error flag, so later calls (e.g. under graph capture)
- * do not allocate. Synchronises `stream` if it has to reallocate. */
+/* Make the workspace of (current device, stream) at least `bytes` long
+ * (take mla_plan(...).workspace_bytes of the largest call to be captured),
+ * so later calls on `stream`, e.g. under graph capture, do not allocate.
+ * Same passages as mla_workspace_bytes. A workspace that a call made under
+ * capture has used is never freed implicitly: if a later eager call on the
+ * stream needs more, the library allocates a larger buffer and parks the
+ * old one (graphs keep replaying with it) until mla_release_workspace. A
+ * buffer no captured call has used is freed on growth, after synchronising
+ * `stream`. Returns a status code. */
 int mla_reserve_workspace(size_t bytes, hipStream_t stream);
+
+/* Free the workspace of (current device, stream) and every buffer parked
+ * for it, after synchronising `stream`. Call it when no graph captured on
+ * `stream` will be replayed again (e.g. before destroying the stream); the
+ * next call on `stream` allocates afresh. Returns a status code. */
+int mla_release_workspace(hipStream_t stream);
 
 /* Draft tree -> ancestor-or-self masks. parents: int32 [batch, q_len] with
  * parents[b,i] in [-1, i-1] (-1 = child of the prefix tail). Bit d of
@@ -251,8 +275,8 @@ int mla_build_tree_mask_host(const int32_t* parents, int batch, int q_len, uint6
  * The target slots must be distinct (two writes to one pool row race).
  * A sequence with an out-of-range length writes nothing and sets
  * MLA_DEVERR_SEQ_LEN; a row whose slot is outside [0, pool_rows) is skipped
- * and sets MLA_DEVERR_SLOT_RANGE. Enqueued on `stream`; allocates nothing
- * but the device error flag on first use. q_len must be in [1, 64]. */
+ * and sets MLA_DEVERR_SLOT_RANGE. Enqueued on `stream`; allocates
+ * nothing. q_len must be in [1, 64]. */
 int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* new_rows, int batch, int q_len,
                   const int32_t* slot_table, const int32_t* seq_lens, hipStream_t stream);
 

@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.mla_workspace_bytes.restype = ctypes.c_size_t
     L.mla_reserve_workspace.argtypes = [ctypes.c_size_t, ctypes.c_void_p]
     L.mla_reserve_workspace.restype = ctypes.c_int
+    L.mla_release_workspace.argtypes = [ctypes.c_void_p]
+    L.mla_release_workspace.restype = ctypes.c_int
     L.mla_build_tree_mask.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_build_tree_mask.restype = ctypes.c_int
     L.mla_build_tree_mask_host.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -270,6 +272,10 @@ def workspace_bytes(batch, q_len, heads, nsplit) -> int:
 
 def reserve_workspace(nbytes: int, stream=None) -> None:
     _check(lib().mla_reserve_workspace(int(nbytes), _stream_handle(stream)), "mla_reserve_workspace")
+
+
+def release_workspace(stream=None) -> None:
+    _check(lib().mla_release_workspace(_stream_handle(stream)), "mla_release_workspace")
 
 
 def build_tree_mask(parents, stream=None):

@@ -1,7 +1,7 @@
 // C-ABI host layer of libmla_verify.so: argument validation, planning
-// (row grouping and split count), per-(device, stream) workspace, device
-// error flag, and kernel launches. Validation runs before any HIP call.
-#include <hip/hip_runtime_api.h>
+// (row grouping and split count), per-(device, stream) workspace, static
+// per-device memory (error flag and zero row), and kernel launches. Validation runs before any HIP call.
+#include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
@@ -10,6 +10,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "mla_internal.h"
 #include "mla_verify.h"
@@ -22,6 +23,17 @@ using mla::kDv;
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ----------------------------------------------------------------- per-device state
+// Static device memory. The GPU runtime gives every device the library runs
+// on its own copy of these arrays, from the first use on that device until
+// the process ends; host code reaches a device's copy only through the
+// address hipGetSymbolAddress returns with that device current (the array
+// names below are host-side stand-ins, not device addresses).
+//   dev_block: the sticky error word at offset 0 and a zero cache row at
+//              kZeroRowOffset (read in place of masked or invalid rows).
+constexpr size_t kDevBlockBytes = 4096;
+constexpr size_t kZeroRowOffset = 256;
+static __device__ __align__(256) unsigned char dev_block[kDevBlockBytes];
+
 struct WsKey {
   int device;
   hipStream_t stream;
@@ -32,11 +44,18 @@ struct WsKey {
 struct WsBuf {
   void* ptr = nullptr;
   size_t bytes = 0;
+  bool captured = false;  // handed to a call made while its stream was capturing
+};
+struct DevPtrs {
+  unsigned* block = nullptr;  // this device's dev_block
 };
 
 std::mutex g_mu;
 std::map<WsKey, WsBuf> g_ws;
-std::map<int, unsigned*> g_err;
+// Buffers replaced by a larger one after a captured call used them: a graph
+// may still replay with them, so only mla_release_workspace frees them.
+std::map<WsKey, std::vector<void*>> g_retired;
+std::map<int, DevPtrs> g_dev;
 std::map<int, int> g_cus;
 
 int current_device(int* dev) {
@@ -59,43 +78,57 @@ bool stream_capturing(hipStream_t s) {
   return st != hipStreamCaptureStatusNone;
 }
 
-// Per-device constant block (allocated and zeroed on first use): the sticky
-// error word at offset 0 and a zero cache row at kZeroRowOffset.
-constexpr size_t kDevBlockBytes = 4096;
-constexpr size_t kZeroRowOffset = 256;
 // Largest batch whose split counts may follow the sequence lengths: the
 // kernels derive them with one sequence per lane of a wavefront.
 constexpr int kBalanceMaxBatch = 64;
 
-int error_word(int dev, hipStream_t stream, unsigned** out) {
+// Device addresses of this device's static arrays, looked up once per device
+// (`dev` must be the current device). Allocates nothing.
+int dev_ptrs(int dev, DevPtrs* out) {
   std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_err.find(dev);
-  if (it != g_err.end()) {
+  auto it = g_dev.find(dev);
+  if (it != g_dev.end()) {
     *out = it->second;
     return MLA_OK;
   }
-  if (stream && stream_capturing(stream)) return MLA_ERR_WORKSPACE;
-  unsigned* p = nullptr;
-  if (hipMalloc(&p, kDevBlockBytes) != hipSuccess) return MLA_ERR_LAUNCH;
-  if (hipMemset(p, 0, kDevBlockBytes) != hipSuccess) return MLA_ERR_LAUNCH;
-  g_err[dev] = p;
-  *out = p;
+  DevPtrs d;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&d.block), HIP_SYMBOL(dev_block)) != hipSuccess || !d.block)
+    return MLA_ERR_LAUNCH;
+  g_dev[dev] = d;
+  *out = d;
   return MLA_OK;
 }
 
+int error_word(int dev, unsigned** out) {
+  DevPtrs d;
+  const int st = dev_ptrs(dev, &d);
+  if (st == MLA_OK) *out = d.block;
+  return st;
+}
+
+// The workspace of (dev, stream), grown to at least `bytes`. A buffer that a
+// call made under capture has used is never freed implicitly: when a later
+// eager call needs more, it is parked until mla_release_workspace.
 int workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lk(g_mu);
-  WsBuf& w = g_ws[WsKey{dev, stream}];
+  const WsKey key{dev, stream};
+  WsBuf& w = g_ws[key];
+  const bool capturing = stream_capturing(stream);
   if (w.bytes >= bytes) {
+    w.captured |= capturing;
     *out = w.ptr;
     return MLA_OK;
   }
-  if (stream_capturing(stream)) return MLA_ERR_WORKSPACE;
+  if (capturing) return MLA_ERR_WORKSPACE;
   if (w.ptr) {
-    if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_LAUNCH;
-    if (hipFree(w.ptr) != hipSuccess) return MLA_ERR_LAUNCH;
-    w.ptr = nullptr;
-    w.bytes = 0;
+    if (w.captured) {
+      g_retired[key].push_back(w.ptr);
+    } else {
+      // only earlier eager calls on this stream can still use it
+      if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_LAUNCH;
+      if (hipFree(w.ptr) != hipSuccess) return MLA_ERR_LAUNCH;
+    }
+    w = WsBuf{};
   }
   // round up to 2 MiB so small growth steps do not reallocate every call
   const size_t want = (bytes + (2u << 20) - 1) & ~((size_t)(2u << 20) - 1);
@@ -106,6 +139,26 @@ int workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
   w.bytes = want;
   *out = w.ptr;
   return MLA_OK;
+}
+
+int release_workspace(int dev, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const WsKey key{dev, stream};
+  auto it = g_ws.find(key);
+  auto rt = g_retired.find(key);
+  if (it == g_ws.end() && rt == g_retired.end()) return MLA_OK;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_LAUNCH;
+  int st = MLA_OK;
+  if (it != g_ws.end()) {
+    if (it->second.ptr && hipFree(it->second.ptr) != hipSuccess) st = MLA_ERR_LAUNCH;
+    g_ws.erase(it);
+  }
+  if (rt != g_retired.end()) {
+    for (void* p : rt->second)
+      if (hipFree(p) != hipSuccess) st = MLA_ERR_LAUNCH;
+    g_retired.erase(rt);
+  }
+  return st;
 }
 
 // ----------------------------------------------------------------- planning
@@ -345,8 +398,10 @@ int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const i
   Call c;
   fill_args(q, kv, slot_table, seq_lens, m, out, lse, &c);
   if ((st = make_plan(q, kv, m, nsplit, device_cus(dev), &c)) != MLA_OK) return st;
-  if ((st = error_word(dev, stream, &c.a.err)) != MLA_OK) return st;
-  c.a.zero_row = reinterpret_cast<const char*>(c.a.err) + kZeroRowOffset;
+  DevPtrs dp;
+  if ((st = dev_ptrs(dev, &dp)) != MLA_OK) return st;
+  c.a.err = dp.block;
+  c.a.zero_row = reinterpret_cast<const char*>(dp.block) + kZeroRowOffset;
   if (c.a.nsplit > 1) {
     void* ws = nullptr;
     if ((st = workspace(dev, stream, c.ws_bytes, &ws)) != MLA_OK) return st;
@@ -394,9 +449,11 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
   if (!plan) return MLA_ERR_INVALID_ARG;
   int st = validate(q, kv_cache, nullptr, nullptr, mask_desc, nullptr, nullptr, nsplit, false);
   if (st != MLA_OK) return st;
+  // the current device's CU count, as the call itself would use (256 when no
+  // device is visible)
   int cus = 256;
   int dev = 0;
-  if (nsplit <= 0 && current_device(&dev) == MLA_OK) cus = device_cus(dev);
+  if (current_device(&dev) == MLA_OK) cus = device_cus(dev);
   Call c;
   if ((st = make_plan(q, kv_cache, mask_desc, nsplit, cus, &c)) != MLA_OK) return st;
   plan->nsplit = c.a.nsplit;
@@ -428,11 +485,18 @@ int mla_reserve_workspace(size_t bytes, hipStream_t stream) {
   int dev = 0;
   int st = current_device(&dev);
   if (st != MLA_OK) return st;
-  unsigned* err = nullptr;
-  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  DevPtrs dp;
+  if ((st = dev_ptrs(dev, &dp)) != MLA_OK) return st;
   if (bytes == 0) return MLA_OK;
   void* p = nullptr;
   return workspace(dev, stream, bytes, &p);
+}
+
+int mla_release_workspace(hipStream_t stream) {
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  return release_workspace(dev, stream);
 }
 
 int mla_build_tree_mask_host(const int32_t* parents, int batch, int q_len, uint64_t* anc_out) {
@@ -460,7 +524,7 @@ int mla_build_tree_mask(const int32_t* parents, int batch, int q_len, uint64_t* 
   int st = current_device(&dev);
   if (st != MLA_OK) return st;
   unsigned* err = nullptr;
-  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  if ((st = error_word(dev, &err)) != MLA_OK) return st;
   return mla::launch_tree_mask(parents, batch, q_len, anc_out, err, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
@@ -475,7 +539,7 @@ int mla_append_kv(void* latent, int64_t pool_rows, int slot_stride, const void* 
   int st = current_device(&dev);
   if (st != MLA_OK) return st;
   unsigned* err = nullptr;
-  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  if ((st = error_word(dev, &err)) != MLA_OK) return st;
   return mla::launch_append(latent, pool_rows, slot_stride, new_rows, batch, q_len, slot_table, seq_lens, err,
                             stream) == hipSuccess
              ? MLA_OK
@@ -493,7 +557,7 @@ int mla_topk_select(const float* scores, int batch, int q_len, int score_stride,
   int st = current_device(&dev);
   if (st != MLA_OK) return st;
   unsigned* err = nullptr;
-  if ((st = error_word(dev, stream, &err)) != MLA_OK) return st;
+  if ((st = error_word(dev, &err)) != MLA_OK) return st;
   void* ws = nullptr;
   if ((st = workspace(dev, stream, mla::topk_workspace_bytes(batch * q_len, score_stride), &ws)) != MLA_OK) return st;
   return mla::launch_topk(scores, batch, q_len, score_stride, seq_lens, topk, topk_idx, err, ws, stream) ==
@@ -530,7 +594,7 @@ int mla_get_device_error(int clear) {
   int st = current_device(&dev);
   if (st != MLA_OK) return st;
   unsigned* err = nullptr;
-  if ((st = error_word(dev, nullptr, &err)) != MLA_OK) return st;
+  if ((st = error_word(dev, &err)) != MLA_OK) return st;
   if (hipDeviceSynchronize() != hipSuccess) return MLA_ERR_LAUNCH;
   unsigned v = 0;
   if (hipMemcpy(&v, err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_LAUNCH;

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 12, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/mla_verify.h but not exported"
-    assert B.abi_version() == 3
+    assert B.abi_version() == 4
 
 
 def test_status_strings(L):
@@ -48,7 +48,8 @@ def test_status_strings(L):
 FAKE = 0x10000
 
 
-def call(q_over=None, kv_over=None, mask_over=None, nsplit=0, out=FAKE, lse=None, slots=FAKE, seq=FAKE):
+def call(q_over=None, kv_over=None, mask_over=None, nsplit=0, out=FAKE, lse=None, slots=FAKE, seq=FAKE,
+         entry="mla_verify_attn"):
     q = dict(data=FAKE, batch=1, q_len=9, heads=8, sm_scale=0.07)
     kv = dict(dtype=B.MLA_KV_BF16, latent=FAKE, rope=None, scale=None, pool_rows=100, slot_stride=50, max_seq_len=0)
     m = dict(kind=1, tree_anc=None, topk_idx=None, topk=0)
@@ -56,7 +57,7 @@ def call(q_over=None, kv_over=None, mask_over=None, nsplit=0, out=FAKE, lse=None
     kv.update(kv_over or {})
     m.update(mask_over or {})
     qd, kd, md = B.MlaQ(**q), B.MlaKV(**kv), B.MlaMask(**m)
-    return B.lib().mla_verify_attn(ctypes.byref(qd), ctypes.byref(kd), slots, seq, ctypes.byref(md), out, lse,
+    return getattr(B.lib(), entry)(ctypes.byref(qd), ctypes.byref(kd), slots, seq, ctypes.byref(md), out, lse,
                                    nsplit, None)
 
 

@@ -79,3 +79,48 @@ def test_graph_replay_topk_matches_eager():
         assert torch.equal(out, ref)
     # the 300-position row is shorter than topk: flagged (and the flag cleared here)
     assert B.device_error() == B.MLA_DEVERR_SEQ_LEN
+
+
+def test_graph_keeps_its_workspace_when_an_eager_call_grows_it():
+    # A graph captured after reserving the workspace keeps replaying with that
+    # buffer: a later, larger eager call on the same stream gets a new buffer
+    # and the captured one stays alive (parked) until it is released.
+    small = I.make_verify("ws_small", batch=1, q_len=9, heads=8, prefixes=[4000], seed=81, layout="random")
+    large = I.workload("c3_64k")
+    ds, dl = DeviceInputs(small), DeviceInputs(large)
+    ref_o, ref_l = ds.run()
+    big_o, big_l = dl.run()
+    torch.cuda.synchronize()
+    p = B.plan(small.batch, small.q_len, small.heads, small.slot_stride, mask=small.mask)
+    s = torch.cuda.Stream()
+    B.reserve_workspace(p["workspace_bytes"], stream=s)
+    out = torch.empty_like(ref_o)
+    lse = torch.empty_like(ref_l)
+    call = B.PreparedCall(ds.q, kv=ds.kv, slot_table=ds.slots, seq_lens=ds.seq_lens, sm_scale=small.sm_scale,
+                          mask=small.mask, out=out, lse=lse)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for rnd in range(2):
+        print(f"[graph] workspace growth round {rnd}", flush=True)
+        # eager call on the capture stream needing a larger workspace
+        with torch.cuda.stream(s):
+            o2, l2 = dl.run()
+        torch.cuda.synchronize()
+        assert torch.equal(o2, big_o) and torch.equal(l2, big_l)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    del g
+    torch.cuda.synchronize()
+    B.release_workspace(stream=s)
+    with torch.cuda.stream(s):
+        o3, l3 = ds.run()              # allocates afresh after the release
+    torch.cuda.synchronize()
+    assert torch.equal(o3, ref_o) and torch.equal(l3, ref_l)
+    assert B.device_error() == 0

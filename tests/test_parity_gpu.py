@@ -54,19 +54,19 @@ def test_c3_64k_random_slots():
     _check(I.workload("c3_64k"), [16, 64, 128, 0])
 
 
-def test_h64_prefix_64k_sampled_heads():
-    # the pages' largest sweep point: q_len 9, H=64, prefix 65536 (every head
-    # computed on the GPU; the oracle checks a sample of them)
+def test_h64_prefix_64k_all_heads():
+    # the pages' largest sweep point: q_len 9, H=64, prefix 65536, compared
+    # over the whole output tensor (all 64 heads)
     # the library's plan: 6 row groups of 6 blocks, 42 splits of 49 tiles
     # with the L2 prefetch; 16 splits: 9 groups of 4, 129 tiles over three
     # 2048-position chunks, prefetching across them
     w = I.workload("sweep_65536")
-    _check(w, [0, 16], heads=[0, 31, 63])
+    _check(w, [0, 16])
 
 
-def test_c4_tree_ragged_sampled_heads():
+def test_c4_tree_ragged_all_heads():
     w = I.workload("c4")
-    _check(w, [0, 8], heads=[0, 17, 63])
+    _check(w, [0, 8])
 
 
 @pytest.mark.parametrize("q_len,heads,prefixes,mask", [
@@ -96,7 +96,7 @@ def test_length_following_splits(heads, prefixes, mask):
     w = I.make_verify(f"balanced_h{heads}_b{len(prefixes)}", batch=len(prefixes), q_len=9, heads=heads,
                       prefixes=prefixes, seed=50 + len(prefixes), layout="random", mask=mask)
     assert B.plan(w.batch, w.q_len, w.heads, w.slot_stride, mask=mask)["balanced"] == 1
-    _check(w, [0], heads=None if heads == 8 else [0, 40, 63])
+    _check(w, [0])
 
 
 def test_repeat_bitwise_and_pool_permutation():
