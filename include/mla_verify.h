@@ -75,6 +75,7 @@ extern "C" {
 #define MLA_ERR_UNSUPPORTED (-3)  /* shape or combination outside what the kernels cover */
 #define MLA_ERR_WORKSPACE (-4)    /* workspace must grow while the stream is being captured */
 #define MLA_ERR_LAUNCH (-5)       /* a HIP call or kernel launch failed */
+#define MLA_ERR_SCRATCH (-6)      /* mla_verify_attn_noalloc: partials exceed its static scratch */
 
 /* Device-side error flag bits (mla_get_device_error). */
 #define MLA_DEVERR_SLOT_RANGE 0x1u   /* slot_table entry outside [0, pool_rows) */
@@ -98,6 +99,8 @@ extern "C" {
 #define MLA_MAX_HEADS 128
 #define MLA_MAX_NSPLIT 1024
 #define MLA_MAX_TOPK 65536
+/* Static scratch of mla_verify_attn_noalloc per device (32 MiB). */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Queries: bf16 [batch, q_len, heads, 576], absorbed (512 latent ++ 64 rope). */
 typedef struct mla_q_t {
@@ -245,6 +248,24 @@ int mla_reserve_workspace(size_t bytes, hipStream_t stream);
  * `stream` will be replayed again (e.g. before destroying the stream); the
  * next call on `stream` allocates afresh. Returns a status code. */
 int mla_release_workspace(hipStream_t stream);
+
+/* No-allocation variant of mla_verify_attn, for callers that cannot call
+ * hipMalloc: code under graph capture with no reserve made, tight serving
+ * loops, harnesses that forbid allocation. Same arguments, same plan, same
+ * kernels and bitwise the same results as mla_verify_attn, but the split
+ * partials live in a static device array of MLA_NOALLOC_SCRATCH_BYTES that
+ * every device the library runs on holds from its first use until the
+ * process ends. Returns MLA_ERR_SCRATCH, launching nothing, when the plan's
+ * workspace_bytes exceed it (e.g. batch 8 x 64 heads x 40 splits); a
+ * smaller nsplit can bring a call under the limit. The call allocates
+ * nothing; the scratch keeps the last call's contents (nothing in it needs
+ * clearing: every call writes the partials it reads). All calls of this
+ * entry point on one device share the one array: calls that overlap on a
+ * device (different streams, or graphs replayed concurrently) race and
+ * give wrong results; order them on one stream. */
+int mla_verify_attn_noalloc(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table,
+                            const int32_t* seq_lens, const mla_mask_t* mask_desc, float* out, float* lse,
+                            int nsplit, hipStream_t stream);
 
 /* Draft tree -> ancestor-or-self masks. parents: int32 [batch, q_len] with
  * parents[b,i] in [-1, i-1] (-1 = child of the prefix tail). Bit d of

@@ -24,6 +24,8 @@ MLA_ERR_ALIGN = -2
 MLA_ERR_UNSUPPORTED = -3
 MLA_ERR_WORKSPACE = -4
 MLA_ERR_LAUNCH = -5
+MLA_ERR_SCRATCH = -6
+MLA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 MLA_DEVERR_SLOT_RANGE = 0x1
 MLA_DEVERR_SEQ_LEN = 0x2
@@ -81,7 +83,7 @@ def lib() -> ctypes.CDLL:
     P = ctypes.POINTER
     attn_args = [P(MlaQ), P(MlaKV), ctypes.c_void_p, ctypes.c_void_p, P(MlaMask), ctypes.c_void_p,
                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    for name in ("mla_verify_attn", "mla_verify_split", "mla_verify_combine"):
+    for name in ("mla_verify_attn", "mla_verify_split", "mla_verify_combine", "mla_verify_attn_noalloc"):
         fn = getattr(L, name)
         fn.argtypes = attn_args
         fn.restype = ctypes.c_int
@@ -194,7 +196,8 @@ def _descs(q, kv_dtype, latent, rope, scale, slot_table, mask, tree_anc, topk_id
     return qd, kd, md, (B, Q, H)
 
 
-_STAGES = {"both": "mla_verify_attn", "split": "mla_verify_split", "combine": "mla_verify_combine"}
+_STAGES = {"both": "mla_verify_attn", "split": "mla_verify_split", "combine": "mla_verify_combine",
+           "noalloc": "mla_verify_attn_noalloc"}
 
 
 def _run(stage, qd, kd, md, slot_table, seq_lens, out, lse, nsplit, stream):

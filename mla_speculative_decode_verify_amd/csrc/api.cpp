@@ -1,6 +1,7 @@
 // C-ABI host layer of libmla_verify.so: argument validation, planning
 // (row grouping and split count), per-(device, stream) workspace, static
-// per-device memory (error flag and zero row), and kernel launches. Validation runs before any HIP call.
+// per-device memory (error flag, zero row, no-allocation scratch), and
+// kernel launches. Validation runs before any HIP call.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -30,9 +31,12 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // names below are host-side stand-ins, not device addresses).
 //   dev_block: the sticky error word at offset 0 and a zero cache row at
 //              kZeroRowOffset (read in place of masked or invalid rows).
+//   scratch:   split partials of mla_verify_attn_noalloc, for callers that
+//              cannot allocate.
 constexpr size_t kDevBlockBytes = 4096;
 constexpr size_t kZeroRowOffset = 256;
 static __device__ __align__(256) unsigned char dev_block[kDevBlockBytes];
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 struct WsKey {
   int device;
@@ -48,6 +52,7 @@ struct WsBuf {
 };
 struct DevPtrs {
   unsigned* block = nullptr;  // this device's dev_block
+  void* scratch = nullptr;    // this device's scratch
 };
 
 std::mutex g_mu;
@@ -94,6 +99,7 @@ int dev_ptrs(int dev, DevPtrs* out) {
   DevPtrs d;
   if (hipGetSymbolAddress(reinterpret_cast<void**>(&d.block), HIP_SYMBOL(dev_block)) != hipSuccess || !d.block)
     return MLA_ERR_LAUNCH;
+  if (hipGetSymbolAddress(&d.scratch, HIP_SYMBOL(scratch)) != hipSuccess || !d.scratch) return MLA_ERR_LAUNCH;
   g_dev[dev] = d;
   *out = d;
   return MLA_OK;
@@ -389,8 +395,13 @@ void fill_args(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, 
 
 enum Stage { kSplit = 1, kCombine = 2, kBoth = 3 };
 
+// Where a call's split partials live: the per-(device, stream) workspace,
+// or this device's static scratch (mla_verify_attn_noalloc).
+enum class Parts { kWorkspace, kScratch };
+
 int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const int32_t* seq_lens,
-        const mla_mask_t* m, float* out, float* lse, int nsplit, hipStream_t stream, int stages) {
+        const mla_mask_t* m, float* out, float* lse, int nsplit, hipStream_t stream, int stages,
+        Parts parts = Parts::kWorkspace) {
   int st = validate(q, kv, slot_table, seq_lens, m, out, lse, nsplit, true);
   if (st != MLA_OK) return st;
   int dev = 0;
@@ -398,13 +409,14 @@ int run(const mla_q_t* q, const mla_kv_t* kv, const int32_t* slot_table, const i
   Call c;
   fill_args(q, kv, slot_table, seq_lens, m, out, lse, &c);
   if ((st = make_plan(q, kv, m, nsplit, device_cus(dev), &c)) != MLA_OK) return st;
+  if (parts == Parts::kScratch && c.ws_bytes > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_SCRATCH;
   DevPtrs dp;
   if ((st = dev_ptrs(dev, &dp)) != MLA_OK) return st;
   c.a.err = dp.block;
   c.a.zero_row = reinterpret_cast<const char*>(dp.block) + kZeroRowOffset;
   if (c.a.nsplit > 1) {
-    void* ws = nullptr;
-    if ((st = workspace(dev, stream, c.ws_bytes, &ws)) != MLA_OK) return st;
+    void* ws = dp.scratch;
+    if (parts == Parts::kWorkspace && (st = workspace(dev, stream, c.ws_bytes, &ws)) != MLA_OK) return st;
     // [fp16 O: P x 512][fp32 LSE: P][fp32 scale: P x 2], P = batch * nsplit * rows;
     // O is split-major per sequence, LSE and scales row-major (splits contiguous)
     const size_t P = (size_t)q->batch * c.a.nsplit * c.a.rows;
@@ -432,6 +444,12 @@ extern "C" {
 int mla_verify_attn(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table, const int32_t* seq_lens,
                     const mla_mask_t* mask_desc, float* out, float* lse, int nsplit, hipStream_t stream) {
   return run(q, kv_cache, slot_table, seq_lens, mask_desc, out, lse, nsplit, stream, kBoth);
+}
+
+int mla_verify_attn_noalloc(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table,
+                            const int32_t* seq_lens, const mla_mask_t* mask_desc, float* out, float* lse,
+                            int nsplit, hipStream_t stream) {
+  return run(q, kv_cache, slot_table, seq_lens, mask_desc, out, lse, nsplit, stream, kBoth, Parts::kScratch);
 }
 
 int mla_verify_split(const mla_q_t* q, const mla_kv_t* kv_cache, const int32_t* slot_table, const int32_t* seq_lens,
@@ -610,6 +628,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported shape or combination";
     case MLA_ERR_WORKSPACE: return "workspace too small while the stream is capturing";
     case MLA_ERR_LAUNCH: return "HIP call or kernel launch failed";
+    case MLA_ERR_SCRATCH: return "split partials exceed the static scratch of mla_verify_attn_noalloc";
     default: return "unknown status";
   }
 }

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert B.status_string(code) and B.status_string(code) != "unknown status"
     assert B.status_string(-99) == "unknown status"
 
@@ -94,10 +94,13 @@ def call(q_over=None, kv_over=None, mask_over=None, nsplit=0, out=FAKE, lse=None
 ])
 def test_bad_arguments_rejected_before_launch(L, kw, code):
     assert call(**kw) == code
+    # the no-allocation variant validates the same way, before any HIP call
+    assert call(entry="mla_verify_attn_noalloc", **kw) == code
 
 
 def test_null_descriptors(L):
     assert L.mla_verify_attn(None, None, None, None, None, None, None, 0, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_verify_attn_noalloc(None, None, None, None, None, None, None, 0, None) == B.MLA_ERR_INVALID_ARG
     assert L.mla_plan(None, None, None, 0, None) == B.MLA_ERR_INVALID_ARG
 
 
