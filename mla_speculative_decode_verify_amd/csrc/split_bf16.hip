@@ -167,8 +167,8 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
 #pragma unroll
     for (int ks = 0; ks < kHalfSteps; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
   }
-  // No wait here: the query loads retire while the slot chunk is staged, and
-  // the wait for the staged slots (issued after them) covers them too.
+  // (the query loads retire while the slot chunk is staged; the drain before
+  // the first gathers makes sure of it)
 
   f32x4 o[kHalfBlocks];
 #pragma unroll
@@ -320,6 +320,11 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
       }
     }
     bad_slot |= lane_bad;
+    // Drain every load the compiler issued (the query loads too): it cannot
+    // see the gathers below, and with any of its own loads still pending it
+    // puts vmcnt waits before the score MFMAs of every tile, which then also
+    // wait for the gathers of the next tiles and undo the lookahead.
+    wait_vmcnt<0>();
     // Row addresses visible to every wave, and whether any slot was invalid.
     // No gather is in flight here (the previous chunk ended with a full
     // drain), so the full barrier costs nothing.

@@ -1,6 +1,5 @@
-// Tile geometry and gather machinery shared by the bf16 split kernels
-// (split_bf16.hip: wavefront pairs per 16-row block; split_quad.hip: four
-// wavefronts sharing every row block). A tile is 32 cache positions whose
+// Tile geometry and gather machinery of the bf16 split kernel
+// (split_bf16.hip). A tile is 32 cache positions whose
 // 576-element bf16 rows are gathered through the page_size = 1 slot table
 // straight into a padded LDS buffer, 16 bytes per lane, by
 // global_load_lds_dwordx4 ("How a CUDA Kernel Designer Discovered That GPU
@@ -68,40 +67,60 @@ struct GatherPlan {
 // or the zero row for positions past the split or with an invalid slot. So
 // a tile never holds stale or poisoned data, and a piece costs one LDS read
 // and one 64-bit add. `lds_base` and `wave` are wave-uniform (scalar).
+// All of the wave's row-address reads are issued before the first load: each
+// load is an asm statement that clobbers memory, so a read placed after one
+// could not be moved ahead of it and every piece would wait out its own LDS
+// round trip.
 template <int NW>
 __device__ __forceinline__ void gather_tile(uint32_t lds_base, int wave, const GatherPlan<NW>& gp,
                                             const char* const* rows_lds, int t_rel) {
   constexpr int kPer = GatherPlan<NW>::kPer;
   const char* const* rows = rows_lds + t_rel;
+  // Piece k exists for every wave when (k + 1) * NW <= kSegments (wave <
+  // NW), a compile-time fact; only the last one needs the run-time test.
+  // With a test (a branch) between two pieces, the compiler consumes each
+  // address read before the next one and every piece waits on LDS alone.
+  auto live = [&](int k) { return (k + 1) * NW <= kSegments || wave + k * NW < kSegments; };
+  uint32_t v[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    if (!(wave + k * NW < kSegments)) continue;  // wave-uniform
-    uint32_t v = gp.packed[k];
+    v[k] = gp.packed[k];
     // Opaque per tile, so the compiler recomputes the source address instead
     // of holding one 64-bit address per piece across the tile loop.
-    asm volatile("" : "+v"(v));
-    const char* row = *reinterpret_cast<const char* const*>(reinterpret_cast<const char*>(rows) + (v & 0xFFFFu));
-    lds_dma_b128(row + (v >> 16), lds_base + (wave + k * NW) * 1024);
+    asm volatile("" : "+v"(v[k]));
+  }
+  // (pieces past the tile point at an in-bounds staged entry, so reading the
+  // address of a piece that is not issued is harmless)
+  const char* src[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    src[k] = *reinterpret_cast<const char* const*>(reinterpret_cast<const char*>(rows) + (v[k] & 0xFFFFu)) +
+             (v[k] >> 16);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (!live(k)) continue;  // wave-uniform
+    lds_dma_b128(src[k], lds_base + (wave + k * NW) * 1024);
   }
 }
 
-// Pull the cache lines of the staged tile at t_rel into L2: waves 0 ..
-// kPfOps - 1 each touch 64 of its 32 x 9 lines with one 4-byte load per
-// lane (the last wave's spare lanes repeat the final line). Rows staged as
-// the zero row touch that row. `wave` is wave-uniform; `plan` is the lane's
-// (line byte offset << 16) | (8 * tile row), from prefetch_plan.
-__device__ __forceinline__ uint32_t prefetch_plan(int wave, int lane) {
-  const int idx = min(wave * 64 + lane, kTile * kRowLines - 1);
+// Pull the cache lines of the staged tile at t_rel into L2: wave loads
+// ("ops") 0 .. kPfOps - 1 each touch 64 of its 32 x 9 lines with one 4-byte
+// load per lane (the last op's spare lanes repeat the final line). Rows
+// staged as the zero row touch that row. `op` is wave-uniform; `plan` is the
+// lane's (line byte offset << 16) | (8 * tile row) for that op, from
+// prefetch_plan.
+__device__ __forceinline__ uint32_t prefetch_plan(int op, int lane) {
+  const int idx = min(op * 64 + lane, kTile * kRowLines - 1);
   const int r = idx / kRowLines, line = idx - r * kRowLines;
   return ((uint32_t)(128 * line) << 16) | (uint32_t)(8 * r);
 }
-__device__ __forceinline__ void prefetch_tile(uint32_t sink_lds, int wave, uint32_t plan,
+__device__ __forceinline__ void prefetch_tile(uint32_t sink_lds, int op, uint32_t plan,
                                               const char* const* rows_lds, int t_rel) {
-  if (wave >= kPfOps) return;
+  if (op >= kPfOps) return;
   asm volatile("" : "+v"(plan));  // recomputed per use rather than held as a 64-bit address
   const char* row =
       *reinterpret_cast<const char* const*>(reinterpret_cast<const char*>(rows_lds + t_rel) + (plan & 0xFFFFu));
-  lds_dma_b32(row + (plan >> 16), sink_lds + wave * 256);
+  lds_dma_b32(row + (plan >> 16), sink_lds + op * 256);
 }
 
 // Positions [lo, hi) of split `split` of S over n positions: the ceil(n / 32)
@@ -135,7 +154,6 @@ __device__ __forceinline__ bf16x8 v_operand(const __bf16* vT0, int d) {
   const bf16x4 hi4 = lds_read_tr16(vT0 + 16 * d + 16 * kLdsStride);
   return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-
 
 }  // namespace tile
 }  // namespace mla
