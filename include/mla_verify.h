@@ -82,6 +82,9 @@ extern "C" {
 #define MLA_DEVERR_SEQ_LEN 0x2u      /* seq_len < q_len (masked kinds) or > slot_stride */
 #define MLA_DEVERR_TREE_PARENT 0x4u  /* parent outside [-1, i-1] in mla_build_tree_mask */
 #define MLA_DEVERR_TOPK_RANGE 0x8u   /* top-k position outside [0, seq_len) */
+#define MLA_DEVERR_SYNC 0x10u        /* a wait between the wavefronts of a workgroup exceeded
+                                        its bound (a library fault: the call's results are
+                                        invalid; raised instead of hanging the GPU) */
 
 /* Cache element types. */
 #define MLA_KV_BF16 0      /* latent: bf16 [pool_rows, 576] (512 latent ++ 64 rope) */

@@ -31,6 +31,7 @@ MLA_DEVERR_SLOT_RANGE = 0x1
 MLA_DEVERR_SEQ_LEN = 0x2
 MLA_DEVERR_TREE_PARENT = 0x4
 MLA_DEVERR_TOPK_RANGE = 0x8
+MLA_DEVERR_SYNC = 0x10
 
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1

@@ -63,6 +63,12 @@ constexpr int kAhead = MLA_KAHEAD;                 // LDS fragments read ahead o
 #endif
 constexpr int kVAhead = MLA_VAHEAD;                // V fragments read ahead of their MFMAs
 
+// Bound on the polls of the pair-exchange wait (each poll sleeps about 64
+// cycles; the partner publishes within a tile, well under a thousand polls).
+// Past it the wave records MLA_DEVERR_SYNC and continues, so a protocol fault
+// can never hang the GPU.
+constexpr int kSpinCap = 1 << 20;
+
 template <int NB, bool kBalanced, bool kPf>
 __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   constexpr int NW = 2 * NB;
@@ -231,8 +237,16 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     // must pass the next tile barrier first.
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial stored before the flag
     if (lane == 0) __hip_atomic_store(&pair_seq[wave], seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(&pair_seq[wave ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != seq)
-      __builtin_amdgcn_s_sleep(1);
+    {
+      int spins = 0;
+      while (__hip_atomic_load(&pair_seq[wave ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != seq) {
+        if (++spins > kSpinCap) {  // a protocol fault: leave (results invalid) rather than hang
+          flag_error(a.err, MLA_DEVERR_SYNC);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
     asm volatile("" ::: "memory");
     // Both halves form half 0 + half 1 (addition commutes exactly), so the
     // pair holds bitwise the same scores.

@@ -44,6 +44,10 @@ constexpr int kRopePieces = kDrope / 8;             // 16-byte bf16 pieces per r
 constexpr int kChunk = 4096;                        // top-k entries staged in LDS at a time
 constexpr float kRescaleSlack = 8.f;
 constexpr int kAhead = 2;                           // LDS fragments read ahead of their MFMAs
+// Bound on the polls of the pair-exchange wait (each poll sleeps about 64
+// cycles; the partner publishes within a tile). Past it the wave records
+// MLA_DEVERR_SYNC and continues, so a protocol fault can never hang the GPU.
+constexpr int kSpinCap = 1 << 20;
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -255,8 +259,16 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
     spart[wave][1][lane] = own1;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial stored before the flag
     if (lane == 0) __hip_atomic_store(&pair_seq[wave], seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(&pair_seq[wave ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != seq)
-      __builtin_amdgcn_s_sleep(1);
+    {
+      int spins = 0;
+      while (__hip_atomic_load(&pair_seq[wave ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != seq) {
+        if (++spins > kSpinCap) {  // a protocol fault: leave (results invalid) rather than hang
+          flag_error(a.err, MLA_DEVERR_SYNC);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
     asm volatile("" ::: "memory");
     // own + partner: addition commutes exactly, so both halves hold bitwise
     // the same sums
