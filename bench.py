@@ -228,20 +228,24 @@ def roofline_entry(w, r):
     def ach(us):
         return cnt["bytes"] / (us * 1e-6) / 1e9 if hbm else cnt["flops"] / (us * 1e-6) / 1e12
 
-    traffic = None
+    traffic = split_traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
         try:
             tr = json.load(open(PROFILE_TRAFFIC))
             key = f"{w.name}/nsplit{r['plan']['nsplit']}"
             if key in tr and tr[key].get("kernel_source_hash") == kernel_hash(w.kind):
                 traffic = tr[key]["bytes_per_launch"]
+                split_traffic = tr[key].get("split_kernel_bytes")
         except Exception:
-            traffic = None
+            traffic = split_traffic = None
+    # traffic: HBM bytes of one call (split + merge kernels, FETCH_SIZE + WRITE_SIZE scaled by a calibration
+    # copy, profiles/traffic.json), null once the kernel sources differ from the profiled ones
     return dict(bound=rf["bound"], achieved=round(ach(r["cold"]), 2), peak=peak,
                 unit="GB/s" if hbm else "TFLOP/s", frac=round(ach(r["cold"]) / peak, 4), traffic=traffic,
                 scope="whole call (split + merge kernels, cold)",
                 split_kernel_us=round(r["split"], 3), split_kernel_achieved=round(ach(r["split"]), 2),
-                split_kernel_frac=round(ach(r["split"]) / peak, 4), roofline_us=round(rf["us"], 3))
+                split_kernel_frac=round(ach(r["split"]) / peak, 4), split_kernel_traffic=split_traffic,
+                roofline_us=round(rf["us"], 3))
 
 
 def cpu_baseline(w, reps=3):
@@ -538,8 +542,9 @@ def bench_absorb(args, w):
 
 
 KERNEL_SOURCES = {
-    "verify": ("split_bf16.hip", "split_epilogue.h", "device_common.h", "mla_internal.h"),
-    "sparse": ("split_fp8.hip", "split_epilogue.h", "device_common.h", "mla_internal.h"),
+    "verify": ("split_bf16.hip", "split_common.h", "split_epilogue.h", "device_common.h", "mla_internal.h",
+               "combine.hip"),
+    "sparse": ("split_fp8.hip", "split_epilogue.h", "device_common.h", "mla_internal.h", "combine.hip"),
 }
 
 
