@@ -152,6 +152,84 @@ def time_calls(calls, steps, warmup, rotate=True):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
+class TimingEvent:
+    """A HIP event used for timing only, created with hipEventDisableSystemFence: recording it performs no
+    system-scope fence, i.e. no L2 write-back and invalidation between the kernels it separates (a default
+    event does one, which adds about 3 µs to each kernel it brackets). Called through the HIP runtime that
+    torch has loaded (same soname)."""
+
+    _lib = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def lib(cls):
+        if cls._lib is None:
+            import ctypes
+
+            import torch  # noqa: F401  (loads the HIP runtime first)
+
+            lib = ctypes.CDLL("libamdhip64.so.7")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._lib = lib
+        return cls._lib
+
+    def __init__(self):
+        import ctypes
+
+        self.h = ctypes.c_void_p()
+        if self.lib().hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self.lib().hipEventRecord(self.h, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end):
+        import ctypes
+
+        ms = ctypes.c_float()
+        if self.lib().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._lib is not None and self.h:
+            self._lib.hipEventDestroy(self.h)
+
+
+def time_stages(split_calls, combine_calls, steps, warmup):
+    """Average µs of the split kernel and of the merge kernel inside a call: each step runs the split stage and
+    then the merge stage of one rotation copy (as one mla_verify_attn call does), with a timing event before,
+    between and after them on the stream the calls run on (torch's current stream). Every step is enqueued
+    behind a GPU sleep, so the host's launch gaps never fall between two events; these are the per-dispatch
+    durations a kernel trace reports. Without a merge (nsplit 1) the second figure is 0."""
+    import torch
+
+    n = len(split_calls)
+    for i in range(warmup):
+        split_calls[i % n]()
+        if combine_calls:
+            combine_calls[i % n]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
+    torch.cuda._sleep(int(1e5) * steps)  # ~40 µs of GPU time (shader clock) per step queued behind it
+    for i in range(steps):
+        ev[i][0].record(stream)
+        split_calls[i % n]()
+        ev[i][1].record(stream)
+        if combine_calls:
+            combine_calls[i % n]()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    split = sum(e[0].elapsed_ms(e[1]) for e in ev) * 1e3 / steps
+    merge = sum(e[1].elapsed_ms(e[2]) for e in ev) * 1e3 / steps if combine_calls else 0.0
+    return split, merge
+
+
 def time_graph(rot, steps, warmup):
     """Average µs per call when the calls (one per rotation copy, in order) are captured into one HIP
     graph and the graph is replayed: no host launch gaps between the kernels. Events on the replay stream."""
@@ -205,9 +283,9 @@ def measure(w, args, nsplit, copies=0, graph=True):
     r = dict(cnt=cnt, copies=copies, plan=plan)
     r["cold"] = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=True)
     r["warm"] = time_calls(rot.calls["both"], args.steps, args.warmup, rotate=False)
-    r["split"] = time_calls(rot.calls["split"], args.steps, args.warmup, rotate=True)
-    r["combine"] = (time_calls(rot.calls["combine"], args.steps, args.warmup, rotate=True)
-                    if plan["nsplit"] > 1 else 0.0)
+    # the split and merge kernels of a cold call, each timed by its own event pair
+    r["split"], r["combine"] = time_stages(rot.calls["split"], rot.calls["combine"] if plan["nsplit"] > 1 else None,
+                                           args.steps, args.warmup)
     r["graph"] = time_graph(rot, args.steps, args.warmup) if graph else None
     log(f"[bench] cold {r['cold']:.2f} us/call, warm {r['warm']:.2f}, split kernel {r['split']:.2f}, "
         f"combine {r['combine']:.2f}, graph replay {r['graph']}")
