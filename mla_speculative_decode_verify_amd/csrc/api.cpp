@@ -221,6 +221,62 @@ struct Layout {
   long key_sets = 1;
 };
 
+// One sequence whose rows fill exactly five 16-row blocks (H=8 with q_len 9
+// or 10, one tensor-parallel rank's share): its rows may go to one
+// workgroup of 5 blocks, 2 of 3 (3 + 2) or 3 of 2 (2 + 2 + 1), the smaller
+// groups gathering every key once each (the second read mostly from L2).
+// Each layout's split + merge kernel time was fitted to batch-1 calls at
+// prefixes 256 to 64k (least squares over 16 to 23 points each, rms error
+// 0.3-0.6 us) as
+//   f + t * T + p * R * S / 1000 + q * G * S * T / 1000
+// with T the tiles of the longest split, R the rows, S the splits and G the
+// groups (the last term: HBM traffic growing with the workgroups in
+// flight). Smaller groups win up to about 32k positions (one tile of 6
+// wavefronts takes 1.55 us where one of 10 takes 1.9, and fewer splits mean
+// fewer partials), one group of 5 beyond (measured: 37.5 us at 64k against
+// 41.4 for 2 x 3 blocks).
+struct FiveBlockFit {
+  int nb;
+  double f, t, p, q;
+};
+constexpr FiveBlockFit kFiveBlockFits[3] = {
+    {5, 13.387, 1.536, 0.510, 0.897}, {3, 12.074, 1.547, 0.302, 0.070}, {2, 12.100, 1.355, 0.137, 0.980}};
+constexpr double kMergeKernelUs = 4.5;  // what a single split saves: no merge kernel
+
+double five_block_cost_us(const FiveBlockFit& fit, int groups, long tiles, long s, long rows) {
+  const long t = (tiles + s - 1) / s;
+  double c = fit.f + fit.t * (double)t + fit.p * (double)(rows * s) / 1000.0 +
+             fit.q * (double)((long)groups * s * t) / 1000.0;
+  if (s == 1) c -= kMergeKernelUs;
+  return c;
+}
+
+Layout plan_five_blocks(int rows, long tiles, int num_cus, int nsplit) {
+  Layout L;
+  double best = 0.0;
+  bool have = false;
+  for (const FiveBlockFit& fit : kFiveBlockFits) {
+    const int groups = (5 + fit.nb - 1) / fit.nb;
+    const long one_pass = std::max<long>(1, num_cus / groups);
+    long lo = 1, hi = std::min(one_pass, tiles);
+    if (nsplit > 0) {
+      if (fit.nb != 5 && (long)nsplit > one_pass) continue;  // the fits hold for one pass of the grid
+      lo = hi = nsplit;
+    }
+    for (long s = lo; s <= hi; ++s) {
+      const double c = five_block_cost_us(fit, groups, tiles, s, rows);
+      if (!have || c < best) {  // the first layout and the fewest splits win ties
+        have = true;
+        best = c;
+        L.nb = fit.nb;
+        L.groups = groups;
+        L.nsplit = (int)std::max<long>(1, std::min<long>(s, MLA_MAX_NSPLIT));
+      }
+    }
+  }
+  return L;
+}
+
 // Row grouping and split count. bf16 verify: all q_len * heads rows of a
 // sequence share its keys, so they form the key set; up to 6 blocks fit one
 // workgroup, else the blocks-per-workgroup and split count come jointly from
@@ -250,6 +306,11 @@ Layout plan_layout(int batch, int q_len, int heads, int keys, int kv_dtype, int 
   const long tiles = std::max<long>(1, ((long)keys + 31) / 32);
   const long rows_total = (long)batch * rows;
   L.key_sets = batch;
+  if (batch == 1 && blocks == 5) {
+    Layout F = plan_five_blocks(rows, tiles, num_cus, nsplit);
+    F.key_sets = batch;
+    return F;
+  }
   double best = 0.0;
   bool have = false;
   for (int nb = 1; nb <= kMaxBlocks; ++nb) {

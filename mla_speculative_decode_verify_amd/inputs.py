@@ -209,6 +209,8 @@ def workload(name: str, seed: Optional[int] = None) -> VerifyInputs:
                 random slots in a 2x pool (seed 5)
     c5          batch 32, q_len 1, H 64, prefix 65536, fp8 latent, top-k 2048 (seed 6)
     sweep_<P>   batch 1, q_len 9, H 64, prefix P, contiguous, causal (seeds 10..14)
+    h8_<P>      batch 1, q_len 9, H 8, prefix P, random slots in a 2x pool, causal
+                (seed 20): the H=8 shape at other prefix lengths
     """
     if name == "c1":
         return make_verify(name, batch=1, q_len=9, heads=8, prefixes=256, seed=seed or 1)
@@ -232,6 +234,9 @@ def workload(name: str, seed: Optional[int] = None) -> VerifyInputs:
         p = int(name.split("_")[1])
         sweep_seeds = {256: 10, 1024: 11, 4096: 12, 16384: 13, 65536: 14}
         return make_verify(name, batch=1, q_len=9, heads=64, prefixes=p, seed=seed or sweep_seeds.get(p, 15))
+    if name.startswith("h8_"):
+        return make_verify(name, batch=1, q_len=9, heads=8, prefixes=int(name.split("_")[1]), seed=seed or 20,
+                           layout="random")
     raise KeyError(name)
 
 

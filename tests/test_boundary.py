@@ -104,17 +104,47 @@ def test_null_descriptors(L):
     assert L.mla_plan(None, None, None, 0, None) == B.MLA_ERR_INVALID_ARG
 
 
+def five_block_cost(nb, tiles, s, rows=72):
+    """The planner's fitted split + merge time of a batch-1 call whose rows fill five 16-row blocks."""
+    f, t, p, q = {5: (13.387, 1.536, 0.510, 0.897), 3: (12.074, 1.547, 0.302, 0.070),
+                  2: (12.100, 1.355, 0.137, 0.980)}[nb]
+    groups = -(-5 // nb)
+    tl = -(-tiles // s)
+    return f + t * tl + p * rows * s / 1000 + q * groups * s * tl / 1000 - (4.5 if s == 1 else 0.0)
+
+
 def test_choose_nsplit_rules(L):
-    # one tensor-parallel rank's share: H=8, q_len 9 -> 72 rows, one row group
-    # 2049 tiles of 32 over at most 256 splits: 9 tiles for the slowest,
-    # and 228 splits already achieve that
-    # (cost: 1.86 us per tile of the slowest split and 8.1 us fixed, plus
-    # 4 us and 0.49 us per MB of partials, 1036 B per split and row, once
-    # there are several splits)
+    # one tensor-parallel rank's share: H=8, q_len 9 -> 72 rows = 5 blocks of
+    # 16. At 64k (2049 tiles of 32) one group of 5 blocks over at most 256
+    # splits: 9 tiles for the slowest, which 228 splits already achieve
     assert B.choose_nsplit(1, 9, 8, 65545, num_cus=256) == 228
+    p = B.plan(1, 9, 8, 65545)
+    assert (p["row_blocks"], p["row_groups"], p["grid"]) == (5, 1, 228)
     assert B.choose_nsplit(1, 9, 8, 65536, num_cus=256) == 256      # 2048 tiles: 8 each
-    assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 171      # 3 tiles each: 5.6 + 6.3 us, 4 tiles: 7.4 + 4.7
-    assert B.choose_nsplit(1, 9, 8, 265, num_cus=256) == 9          # one tile each
+    # at 16k (513 tiles) two groups (3 + 2 blocks) of 103 splits, 5 tiles
+    # each, beat one group of 171 splits with 3 tiles each (measured 22.4
+    # against 25.6 us of split + merge kernel time)
+    assert B.choose_nsplit(1, 9, 8, 16393, num_cus=256) == 103
+    p = B.plan(1, 9, 8, 16393)
+    assert (p["row_blocks"], p["row_groups"], p["grid"]) == (3, 2, 206)
+    assert five_block_cost(3, 513, 103) < five_block_cost(5, 513, 171)
+    # up to 4k three groups of 2 blocks: prefix 256 (9 tiles) one tile each
+    p = B.plan(1, 9, 8, 265)
+    assert (p["nsplit"], p["row_blocks"], p["row_groups"], p["grid"]) == (9, 2, 3, 27)
+    p = B.plan(1, 9, 8, 4105)
+    assert (p["nsplit"], p["row_blocks"], p["row_groups"], p["grid"]) == (65, 2, 3, 195)
+    # every layout and split count the planner could take costs at least as
+    # much under the fits as the one it took
+    for n in (265, 1033, 4105, 8201, 16393, 32777, 65545):
+        tiles = -(-n // 32)
+        p = B.plan(1, 9, 8, n)
+        chosen = five_block_cost(p["row_blocks"], tiles, p["nsplit"])
+        for nb in (5, 3, 2):
+            for s in range(1, min(256 // -(-5 // nb), tiles) + 1):
+                assert chosen <= five_block_cost(nb, tiles, s) + 1e-9, (n, nb, s)
+    # an explicit split count keeps one pass of the grid for the smaller groups
+    assert B.plan(1, 9, 8, 16393, nsplit=129)["row_groups"] == 1
+    assert B.plan(1, 9, 8, 16393, nsplit=128)["row_groups"] == 2
     # H=64 short: 9 row groups of 4 blocks, at most 28 splits (252
     # workgroups, one wave); 129 tiles need 5 per split, which 26 splits give
     assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 26
@@ -137,17 +167,20 @@ def test_choose_nsplit_rules(L):
     assert B.plan(1, 9, 8, 65545, nsplit=64)["l2_prefetch"] == 1   # 33 tiles each
     assert B.plan(1, 9, 8, 65545, nsplit=86)["l2_prefetch"] == 1   # 2049 tiles: 24 in the longest
     assert B.plan(1, 9, 8, 65545, nsplit=90)["l2_prefetch"] == 0   # 23
-    assert B.choose_nsplit(1, 9, 8, 100, num_cus=256) == 4          # 4 tiles: 7.4 us alone, 1.9 + 4.1 split
-    assert B.choose_nsplit(1, 9, 8, 32, num_cus=256) == 1
+    assert B.choose_nsplit(1, 9, 8, 32, num_cus=256) == 1           # one tile: no merge
     assert B.choose_nsplit(32, 1, 64, 2048, kv_dtype=B.MLA_KV_FP8_E4M3, num_cus=256) == 8
     for args in [(0, 9, 8, 10, 0, 256), (1, 9, 8, -1, 0, 256), (1, 9, 8, 10, 5, 256), (1, 9, 8, 10, 0, 0)]:
         assert L.mla_choose_nsplit(*args) == B.MLA_ERR_INVALID_ARG
 
 
 def test_plan_shapes(L):
-    p = B.plan(1, 9, 8, 16393, nsplit=64)      # 72 rows: 5 blocks of 16, two wavefronts each
-    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (64, 10, 1, 64, 5)
+    # 72 rows: 5 blocks of 16, two wavefronts each; with 64 splits three
+    # groups of 2 blocks (the last one half empty) fit one pass of the grid
+    p = B.plan(1, 9, 8, 16393, nsplit=64)
+    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (64, 4, 3, 192, 2)
     assert p["workspace_bytes"] == 64 * 72 * 1036 + 4
+    p = B.plan(1, 9, 8, 16393, nsplit=200)
+    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (200, 10, 1, 200, 5)
     p = B.plan(1, 9, 64, 4105, nsplit=16)
     assert (p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (8, 9, 144, 4)
     # 144 rows = 9 blocks: one pass of the grid either way, so 3 groups of 4

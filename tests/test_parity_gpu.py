@@ -191,9 +191,10 @@ def test_partials_keep_value_range(factor):
 
 def test_mixed_plans_share_the_workspace():
     # Calls with different plans run back to back on one stream and share the
-    # library's workspace: uniform splits with one 5-block group (H=8),
-    # length-following splits with 6-block groups and the L2 prefetch (ragged
-    # tree batch, H=64), 8 groups of 5 blocks (H=64), and the fp8 sparse path.
+    # library's workspace: uniform splits with two groups of 3 blocks (H=8 at
+    # 9k) and with one 5-block group (H=8 at 60k), length-following splits
+    # with 6-block groups and the L2 prefetch (ragged tree batch, H=64), 8
+    # groups of 5 blocks (H=64), and the fp8 sparse path.
     # Each result must equal, bit for bit, the same call made first on its
     # own, whatever ran between (stale split counts or partials would show).
     import numpy as np
@@ -204,6 +205,7 @@ def test_mixed_plans_share_the_workspace():
                       layout="random", mask="tree"),
         I.make_verify("mix_h64", batch=1, q_len=9, heads=64, prefixes=[16000], seed=63, layout="contiguous"),
         I.workload("c5"),
+        I.make_verify("mix_h8_long", batch=1, q_len=9, heads=8, prefixes=[60000], seed=64, layout="random"),
     ]
     devs = [DeviceInputs(w) for w in shapes]
     first = []
@@ -211,11 +213,12 @@ def test_mixed_plans_share_the_workspace():
         o, l = d.run()
         torch.cuda.synchronize()
         first.append((o.clone(), l.clone()))
-    plans = [B.plan(w.batch, w.q_len, w.heads, w.slot_stride, mask=w.mask) for w in shapes[:3]]
-    assert plans[0]["row_blocks"] == 5 and plans[0]["balanced"] == 0
+    plans = [B.plan(w.batch, w.q_len, w.heads, w.slot_stride, mask=w.mask) for w in shapes[:3] + shapes[4:]]
+    assert plans[0]["row_blocks"] == 3 and plans[0]["row_groups"] == 2 and plans[0]["balanced"] == 0
     assert plans[1]["balanced"] == 1 and plans[1]["row_blocks"] == 6 and plans[1]["l2_prefetch"] == 1
     assert plans[2]["row_blocks"] == 5 and plans[2]["row_groups"] == 8
-    order = [1, 0, 3, 2, 1, 3, 0, 2, 1]
+    assert plans[3]["row_blocks"] == 5 and plans[3]["row_groups"] == 1
+    order = [1, 0, 4, 3, 2, 1, 3, 0, 4, 2, 1]
     for k in order:
         _log(f"[mixed] {shapes[k].name}")
         o, l = devs[k].run()
