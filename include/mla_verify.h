@@ -213,7 +213,12 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
  * workgroup), 8 us fixed (11.4 us with six blocks), and, when s > 1, 4 us
  * for the merge plus 0.49 us per MB of partials (1036 bytes per split and
  * query row, written and read back); the cheapest wins, the fewest splits on
- * ties. For an fp8 cache, as many as fit, with at least 128 list entries
+ * ties. A single sequence whose rows fill exactly five blocks (e.g. 8 heads,
+ * q_len 9) may instead be dealt to two groups of three blocks or three of
+ * two, chosen with the count by split + merge times fitted per layout (the
+ * smaller groups win below about 32k positions: fewer wavefronts per SIMD
+ * make a tile cheaper, fewer splits make fewer partials). mla_plan reports
+ * the layout taken. For an fp8 cache, as many as fit, with at least 128 list entries
  * per split. max_seq_len is the longest sequence for a bf16 cache and the
  * top-k list length for an fp8 cache (each query's list is split). ("How
  * One Environment Variable Unlocked 3x Throughput", section "The Occupancy
