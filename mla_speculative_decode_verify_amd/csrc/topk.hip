@@ -9,19 +9,20 @@
 // marks a position past the row's length, which is never counted.
 //
 // A row is cut into parts of 8192 positions, one 256-thread workgroup each,
-// so every CU takes part even with few rows. Four kernels:
+// so every CU takes part even with few rows. Three kernels:
 //   1. hist:  per part, the histogram of the keys' top 11 bits;
 //   2. cands: per part, the bin B0 where the row's count from the top
 //             reaches topk (from all parts' histograms); the part counts its
 //             keys above B0 and appends those inside B0 (key, position) to
 //             the row's candidate list;
-//   3. select: per row, a radix select over the candidates' remaining 21
+//   3. write: per part, first the selection (every part of a row computes
+//             the same): a radix select over the candidates' remaining 21
 //             bits (11 + 10) finds the topk-th largest key and how many of
-//             the keys equal to it are kept; then, in part order, each part
-//             gets its output offset and its share of those ties;
-//   4. write: per part, the selected positions in ascending order, each
-//             wavefront taking a contiguous quarter of the part and every
-//             16-byte-load block ordered by a prefix sum over lanes.
+//             the keys equal to it are kept, and, in part order, this part's
+//             output offset and its share of those ties; then the selected
+//             positions in ascending order, each wavefront taking a
+//             contiguous quarter of the part and every 16-byte-load block
+//             ordered by a prefix sum over lanes.
 #include "device_common.h"
 #include "mla_internal.h"
 #include "mla_verify.h"
@@ -34,7 +35,6 @@ constexpr int kPartThreads = 256;
 constexpr int kPartWaves = kPartThreads / 64;
 constexpr int kPart = 8192;                          // positions per part
 constexpr int kPartBlocks = kPart / kPartWaves / 256;  // 256-position blocks per wavefront (8)
-constexpr int kSelThreads = 1024;
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -236,16 +236,17 @@ __global__ __launch_bounds__(kPartThreads) void topk_cands_kernel(const float* s
     }
 }
 
-// ---- 3. exact threshold from the candidates, then per-part offsets and tie shares
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(int score_stride, const int32_t* seq_lens,
-                                                                  int q_len, int topk, TopkWs ws) {
-  __shared__ uint32_t total[2048];  // one histogram: the candidates spread over its bins
-  __shared__ uint32_t res[3];
-  __shared__ uint32_t gt[128], eq[128];  // per part: keys above / candidates equal to the threshold
-  const int row = blockIdx.x, b = row / q_len;
+// ---- 3. exact threshold from the candidates, then this part's output offset
+// and tie share. Every part's workgroup of the write kernel computes it from
+// the row's candidates (all get the same values), which costs each a few
+// microseconds of LDS work but saves a kernel launch and its round trips.
+struct RowSelect {
+  uint32_t thr, off, ties;
+};
+__device__ RowSelect row_select(int row, int n, int part, const TopkWs& ws, uint32_t* total, uint32_t* res,
+                                uint32_t* gt, uint32_t* eq, uint32_t* out3) {
+  constexpr int NT = kPartThreads;
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int n = row_len(seq_lens, b, score_stride);
-  if (n <= topk) return;
   const uint32_t m = ws.row_info[row * 4 + 0];
   const uint32_t b0 = ws.row_info[row * 4 + 1];
   uint32_t rem = ws.row_info[row * 4 + 2];
@@ -257,9 +258,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(int score_stri
     const int shift = pass == 0 ? 10 : 0;
     const uint32_t known = pass == 0 ? 0xFFE00000u : 0xFFFFFC00u;  // bits fixed so far
     const int nbins = pass == 0 ? 2048 : 1024;
-    for (int j = tid; j < 2048; j += kSelThreads) total[j] = 0;
+    for (int j = tid; j < 2048; j += NT) total[j] = 0;
     __syncthreads();
-    for (uint32_t c = tid; c < m; c += kSelThreads) {
+    for (uint32_t c = tid; c < m; c += NT) {
       const uint32_t k = cand[2 * c];
       if ((k & known) == prefix) atomicAdd(&total[(k >> shift) & (nbins - 1)], 1u);
     }
@@ -268,35 +269,35 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(int score_stri
     __syncthreads();
     prefix |= res[0] << shift;
     rem = res[1];
-    __syncthreads();  // res and the histograms are rewritten by the next pass
+    __syncthreads();  // res and the histogram are rewritten by the next pass
   }
   const uint32_t thr = prefix;  // the topk-th largest key; keep `rem` of the keys equal to it
   const int parts_used = (n + kPart - 1) / kPart;
-  for (int q = tid; q < 128; q += kSelThreads) {
+  for (int q = tid; q < 128; q += NT) {
     gt[q] = 0;
     eq[q] = 0;
   }
   __syncthreads();
-  for (uint32_t c = tid; c < m; c += kSelThreads) {
+  for (uint32_t c = tid; c < m; c += NT) {
     const uint32_t k = cand[2 * c], q = cand[2 * c + 1] / kPart;
     if (k > thr) atomicAdd(&gt[q], 1u);
     if (k == thr) atomicAdd(&eq[q], 1u);
   }
-  // keys above B0 per part, loaded by all threads at once (gt holds them too)
-  uint32_t* pc_row = ws.part_cnt + (size_t)row * ws.parts * 3;
-  for (int q = tid; q < parts_used; q += kSelThreads) atomicAdd(&gt[q], pc_row[q * 3 + 0]);
+  // keys above B0 per part (counted by the cands kernel)
+  const uint32_t* pc_row = ws.part_cnt + (size_t)row * ws.parts * 3;
+  for (int q = tid; q < parts_used; q += NT) atomicAdd(&gt[q], pc_row[q * 3 + 0]);
   __syncthreads();
   if (tid == 0) {
     uint32_t off = 0, eq_before = 0;
-    for (int q = 0; q < parts_used; ++q) {
-      const uint32_t share = eq_before >= rem ? 0u : min(eq[q], rem - eq_before);
-      pc_row[q * 3 + 1] = off;
-      pc_row[q * 3 + 2] = share;
-      off += gt[q] + share;
+    for (int q = 0; q < part; ++q) {
+      off += gt[q] + (eq_before >= rem ? 0u : min(eq[q], rem - eq_before));
       eq_before += eq[q];
     }
-    ws.row_info[row * 4 + 1] = thr;  // the write kernel reads the threshold here
+    out3[0] = off;
+    out3[1] = eq_before >= rem ? 0u : min(eq[part], rem - eq_before);
   }
+  __syncthreads();
+  return RowSelect{thr, out3[0], out3[1]};
 }
 
 // ---- 4. selected positions of a part, in ascending order
@@ -304,6 +305,9 @@ __global__ __launch_bounds__(kPartThreads) void topk_write_kernel(const float* s
                                                                   const int32_t* seq_lens, int q_len, int topk,
                                                                   int32_t* out, unsigned* err, TopkWs ws) {
   __shared__ uint32_t wcnt[kPartWaves][2];
+  __shared__ uint32_t total[2048];
+  __shared__ uint32_t res[3], out3[2];
+  __shared__ uint32_t gt[128], eq[128];  // per part: keys above / candidates equal to the threshold
   const int part = blockIdx.x, row = blockIdx.y, b = row / q_len;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t* o = out + (size_t)row * topk;
@@ -318,11 +322,10 @@ __global__ __launch_bounds__(kPartThreads) void topk_write_kernel(const float* s
   }
   if (part * kPart >= n) return;
   if (part == 0 && threadIdx.x == 0 && n_raw > score_stride) flag_error(err, MLA_DEVERR_SEQ_LEN);
-  const uint32_t thr = ws.row_info[row * 4 + 1];
-  const uint32_t* pc = ws.part_cnt + ((size_t)row * ws.parts + part) * 3;
-  const uint32_t part_off = pc[1], part_ties = pc[2];
   uint32_t key[kPartBlocks][4];
-  load_part(scores + (size_t)row * score_stride, part, n, key);
+  load_part(scores + (size_t)row * score_stride, part, n, key);  // in flight during the selection
+  const RowSelect sel = row_select(row, n, part, ws, total, res, gt, eq, out3);
+  const uint32_t thr = sel.thr, part_off = sel.off, part_ties = sel.ties;
   uint32_t above = 0, n_eq = 0;
 #pragma unroll
   for (int j = 0; j < kPartBlocks; ++j)
@@ -401,8 +404,6 @@ hipError_t launch_topk(const float* scores, int batch, int q_len, int score_stri
                      q_len, topk, ws);
   hipLaunchKernelGGL(topk_cands_kernel, parts_grid, dim3(kPartThreads), 0, stream, scores, score_stride, seq_lens,
                      q_len, topk, ws);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, score_stride, seq_lens, q_len,
-                     topk, ws);
   hipLaunchKernelGGL(topk_write_kernel, parts_grid, dim3(kPartThreads), 0, stream, scores, score_stride, seq_lens,
                      q_len, topk, out, err, ws);
   return hipGetLastError();
