@@ -138,7 +138,9 @@ typedef struct mla_plan_t {
   int nsplit;            /* KV splits per sequence actually used */
   int waves_per_group;   /* wavefronts per workgroup (two per 16-row query block) */
   int row_groups;        /* workgroups along the query-row axis per split */
-  int grid;              /* split-kernel workgroups */
+  int grid;              /* split-kernel workgroups with work (the launch adds
+                            idle ones up to a multiple of 8, and up to whole
+                            splits per XCD when that still fits the CUs) */
   size_t workspace_bytes;/* partial storage needed (0 when nsplit == 1) */
   int kernel;            /* 0 = bf16 verify, 1 = fp8 top-k sparse */
   int row_blocks;        /* 16-row query blocks per workgroup */

@@ -411,6 +411,18 @@ int make_plan(const mla_q_t* q, const mla_kv_t* kv, const mla_mask_t* m, int nsp
   // workgroup units of the 1-D split grid, indexed with int on the device
   const long units = (c->a.balance_units > 0 ? c->a.balance_units : key_sets * s) * c->groups;
   if (units > 0x7fffffffL - 8) return MLA_ERR_UNSUPPORTED;
+  // Units k * groups + g go to the XCDs in contiguous runs of xcd_chunk (the
+  // kernels' xcd_unit). A run that is a multiple of the row groups keeps all
+  // groups of a split, which gather the same cache rows, on one XCD and its
+  // L2. That is used when the padded grid still fits the XCDs' CUs in one
+  // pass and still spreads the work over all 8 XCDs (idle padding units
+  // return at once).
+  long chunk = (units + 7) / 8;
+  if (c->groups > 1) {
+    const long aligned = (chunk + c->groups - 1) / c->groups * c->groups;
+    if (aligned * 8 <= num_cus && units > 7 * aligned) chunk = aligned;
+  }
+  c->a.xcd_chunk = (int)chunk;
   c->a.nsplit = s;
   c->ws_bytes = mla_workspace_bytes(q->batch, q->q_len, q->heads, s);
   // L2 prefetch ahead of the gathers pays only for long splits (the kernel

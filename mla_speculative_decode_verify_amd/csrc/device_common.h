@@ -116,7 +116,11 @@ __device__ __forceinline__ int xcd_unit(int units) {
   const int j = (L % kXcds) * C + L / kXcds;
   return j < units ? j : -1;
 }
-inline unsigned xcd_grid(long units) { return (unsigned)(((units + kXcds - 1) / kXcds) * kXcds); }
+// Grid for `units` work units: 8 * C workgroups, C = max(ceil(units / 8), chunk).
+inline unsigned xcd_grid(long units, long chunk = 0) {
+  const long c = (units + kXcds - 1) / kXcds;
+  return (unsigned)((c > chunk ? c : chunk) * kXcds);
+}
 
 // Sum / max over the 64 lanes, every lane getting the result, in VALU
 // cross-lane moves only (no LDS permute): DPP swaps within quads, then

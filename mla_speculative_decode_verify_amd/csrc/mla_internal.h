@@ -46,6 +46,9 @@ struct Args {
   int balance_units;        // > 0: per-sequence split counts follow the lengths
                             // (balanced_split), with at most this many splits in all
   int row_groups;           // workgroups along the row axis (set at launch)
+  int xcd_chunk;            // work units per XCD (grid = 8 * xcd_chunk, at least ceil(units / 8)):
+                            // a multiple of row_groups when that still gives every XCD no more
+                            // workgroups than CUs, so all row groups of a split share one L2
   int l2_prefetch;          // bf16 split kernel: pull cache lines into L2 a few tiles ahead of
                             // the gathers (long splits only; set by the plan)
   int mask_kind;

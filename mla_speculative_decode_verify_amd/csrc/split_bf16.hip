@@ -391,9 +391,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
 template <int NB, bool kPf>
 hipError_t launch_nb_pf(const Args& b, long units, hipStream_t stream) {
   if (b.balance_units > 0)
-    hipLaunchKernelGGL((split_bf16_kernel<NB, true, kPf>), dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
+    hipLaunchKernelGGL((split_bf16_kernel<NB, true, kPf>), dim3(xcd_grid(units, b.xcd_chunk)), dim3(NB * 128), 0, stream, b);
   else
-    hipLaunchKernelGGL((split_bf16_kernel<NB, false, kPf>), dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
+    hipLaunchKernelGGL((split_bf16_kernel<NB, false, kPf>), dim3(xcd_grid(units, b.xcd_chunk)), dim3(NB * 128), 0, stream, b);
   return hipGetLastError();
 }
 

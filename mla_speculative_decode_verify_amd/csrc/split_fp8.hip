@@ -393,7 +393,7 @@ hipError_t launch_nb(const Args& a, int row_groups, hipStream_t stream) {
   Args b = a;
   b.row_groups = row_groups;
   const long units = (long)a.batch * a.q_len * a.nsplit * row_groups;
-  hipLaunchKernelGGL(split_fp8_topk_kernel<NB>, dim3(xcd_grid(units)), dim3(NB * 128), 0, stream, b);
+  hipLaunchKernelGGL(split_fp8_topk_kernel<NB>, dim3(xcd_grid(units, b.xcd_chunk)), dim3(NB * 128), 0, stream, b);
   return hipGetLastError();
 }
 
