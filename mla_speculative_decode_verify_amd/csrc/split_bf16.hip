@@ -37,6 +37,8 @@
 // The running max is updated lazily: the exponent base only moves (and the
 // accumulators are only rescaled) when some row's max grows by more than
 // kRescaleSlack in log2 units, so weights stay below 2^kRescaleSlack.
+#include <type_traits>
+
 #include "device_common.h"
 #include "mla_internal.h"
 #include "mla_verify.h"
@@ -63,6 +65,20 @@ constexpr int kAhead = MLA_KAHEAD;                 // LDS fragments read ahead o
 #endif
 constexpr int kVAhead = MLA_VAHEAD;                // V fragments read ahead of their MFMAs
 
+// Gather-only wavefronts per workgroup. With an odd number of blocks the
+// pairs leave SIMDs 2 and 3 one wavefront short of SIMDs 0 and 1 (wavefront w
+// runs on SIMD w % 4), and a SIMD's LDS reads and MFMAs barely overlap, so
+// the SIMDs that hold three pairs' halves set the tile time. Two extra
+// wavefronts, which land on SIMDs 2 and 3, then issue every gather and L2
+// prefetch (and read their row addresses from LDS) in place of the pairs.
+#ifndef MLA_GATHER_WAVES
+#define MLA_GATHER_WAVES 1
+#endif
+template <int NB>
+constexpr int kGatherWaves = (MLA_GATHER_WAVES && NB % 2 == 1) ? 2 : 0;
+template <int NB>
+constexpr int kThreads = (2 * NB + kGatherWaves<NB>) * 64;
+
 // Bound on the polls of the pair-exchange wait (each poll sleeps about 64
 // cycles; the partner publishes within a tile, well under a thousand polls).
 // Past it the wave records MLA_DEVERR_SYNC and continues, so a protocol fault
@@ -70,12 +86,15 @@ constexpr int kVAhead = MLA_VAHEAD;                // V fragments read ahead of 
 constexpr int kSpinCap = 1 << 20;
 
 template <int NB, bool kBalanced, bool kPf>
-__global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
-  constexpr int NW = 2 * NB;
-  // Fewest gather instructions any wave issues per tile: waiting until at
-  // most that many are outstanding proves tile t has landed whenever tile
-  // t+1 was issued after it (loads retire in order).
-  constexpr int kWaitAhead = (kSegments / NW) < 63 ? (kSegments / NW) : 63;
+__global__ __launch_bounds__(kThreads<NB>, 1) void split_bf16_kernel(Args a) {
+  constexpr int NW = 2 * NB;             // compute wavefronts (a pair per block)
+  constexpr int NG = kGatherWaves<NB>;   // gather-only wavefronts after them
+  constexpr int NGW = NG > 0 ? NG : NW;  // wavefronts that issue the gathers
+  constexpr int NT = NW + NG;
+  // Fewest gather instructions any gathering wave issues per tile: waiting
+  // until at most that many are outstanding proves tile t has landed
+  // whenever tile t+1 was issued after it (loads retire in order).
+  constexpr int kWaitAhead = (kSegments / NGW) < 63 ? (kSegments / NGW) : 63;
   __shared__ __attribute__((aligned(16))) __bf16 kv[kStages * kBufElems];  // tile ring
   __shared__ __attribute__((aligned(16))) f32x4 spart[NW][2][64];          // partial scores per wave
   __shared__ const char* rows_lds[kSlotChunk + kTile];                     // cache-row addresses of the chunk
@@ -120,7 +139,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   // and are used only if the true range turns out the same, so the slot
   // loads no longer wait behind the length load (uniform counts only: with
   // length-following counts the length is already known)
-  constexpr int kBatch = NW * 64;  // slot loads per staging pass and unroll step
+  constexpr int kBatch = NT * 64;  // slot loads per staging pass and unroll step
   int lo_h = 0, hi_h = 0;
   if (!kBalanced) split_range(a.len_hint, S, split, lo_h, hi_h);
   int v_h[8];
@@ -150,11 +169,10 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const char* pool = static_cast<const char*>(a.latent);
   const char* zero_row = static_cast<const char*>(a.zero_row);
   const uint32_t pool_lim = (uint32_t)min<int64_t>(a.pool_rows, (int64_t)1 << 31);
-  const GatherPlan<NW> gp(wave, lane);
-  const uint32_t pf_plan = prefetch_plan(wave, lane);
   // uniform; the instantiation without prefetch keeps the registers its
   // plan would take (short splits, where the prefetch does not pay)
   const bool pf_on = kPf && kPfAhead > 2 && hi - lo >= kPfMinKeys;
+  const bool gather_only = NG > 0 && wave >= NW;  // wave-uniform
 
   // ---- this wavefront's rows, draft-mask words and query k-steps
   const int row0 = (grp * NB + blk) * 16;
@@ -167,7 +185,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const uint32_t anc_lo = (uint32_t)bits, anc_hi = (uint32_t)(bits >> 32);
 
   bf16x8 qr[kHalfSteps];
-  {
+  if (!gather_only) {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)b * R + min(row, R - 1)) * kDk +
                        32 * kHalfSteps * half + 8 * g;
 #pragma unroll
@@ -189,7 +207,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
   const int offA = li * kLdsStride + 32 * kHalfSteps * half + 8 * g;
   const int offV = (4 * g + (li >> 2)) * kLdsStride + 256 * half + 4 * (li & 3);
 
-  if (lane == 0) __hip_atomic_store(&pair_seq[wave], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (lane == 0 && !gather_only) __hip_atomic_store(&pair_seq[wave], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   int seq = 0;                         // tiles processed by this workgroup
 
   // chunk_bad: the staged chunk holds an invalid slot, so every tile of it
@@ -311,68 +329,110 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
     }
   };
 
-  // ---- main loop: chunks of up to kSlotChunk positions, tiles pipelined two ahead
-  for (int cb = lo; cb < hi; cb += kSlotChunk) {
-    const int ce = min(hi, cb + kSlotChunk);
-    // stage the chunk's row addresses (batches of 8 slot loads per thread in
-    // flight at once), plus kTile zero-row entries past its end
-    bool lane_bad = false;
-    for (int i0 = 0; i0 < ce - cb + kTile; i0 += 8 * kBatch) {
-      int v[8];
-      const bool early = hint_ok && cb == lo && i0 == 0;
+  // ---- main loop: chunks of up to kSlotChunk positions, tiles pipelined two
+  // ahead. kGather / kCompute select a wavefront's roles: with gather-only
+  // wavefronts (NG > 0) those issue every gather and prefetch and the pairs
+  // only compute; otherwise every wavefront does both. Both roles meet at the
+  // same barriers: one per chunk after the staging, one per tile, one at the
+  // chunk's end.
+  auto main_loop = [&](auto gather_role, auto compute_role) {
+    constexpr bool kGather = decltype(gather_role)::value;
+    constexpr bool kCompute = decltype(compute_role)::value;
+    const int gw = NG > 0 ? wave - NW : wave;  // index among the gathering wavefronts
+    GatherPlan<NGW> gp(kGather ? gw : 0, lane);
+    // prefetch ops of one tile this wavefront issues: gw, gw + NGW, ...
+    constexpr int kPfPer = (kPfOps + NGW - 1) / NGW;
+    uint32_t pf_plan[kPfPer];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kBatch + tid;
-        v[u] = i < ce - cb ? (early ? v_h[u] : slot_row[cb + i]) : -1;
-      }
+    for (int k = 0; k < kPfPer; ++k) pf_plan[k] = prefetch_plan(min(gw + k * NGW, kPfOps - 1), lane);
+    auto prefetch = [&](uint32_t sink, int t_rel) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kBatch + tid;
-        const bool ok = (uint32_t)v[u] < pool_lim;
-        lane_bad |= (i < ce - cb) && !ok;
-        if (i < ce - cb + kTile) rows_lds[i] = ok ? pool + (size_t)(uint32_t)v[u] * (kDk * 2) : zero_row;
-      }
-    }
-    bad_slot |= lane_bad;
-    // Drain every load the compiler issued (the query loads too): it cannot
-    // see the gathers below, and with any of its own loads still pending it
-    // puts vmcnt waits before the score MFMAs of every tile, which then also
-    // wait for the gathers of the next tiles and undo the lookahead.
-    wait_vmcnt<0>();
-    // Row addresses visible to every wave, and whether any slot was invalid.
-    // No gather is in flight here (the previous chunk ended with a full
-    // drain), so the full barrier costs nothing.
-    const bool chunk_bad = __syncthreads_or(lane_bad) != 0;
-    const uint32_t kv_lds = lds_addr_of(kv);
-    const uint32_t sink_lds = lds_addr_of(pf_sink);
-    gather_tile<NW>(kv_lds, wave, gp, rows_lds, 0);
-    if (cb + kTile < ce) gather_tile<NW>(kv_lds + kBufElems * 2, wave, gp, rows_lds, kTile);
-    // tiles 2 .. kPfAhead - 1 of the chunk, before the loop prefetches the rest
-    if (pf_on) {
+      for (int k = 0; k < kPfPer; ++k)
+        if (gw + k * NGW < kPfOps) prefetch_tile(sink, gw + k * NGW, pf_plan[k], rows_lds, t_rel);
+    };
+    for (int cb = lo; cb < hi; cb += kSlotChunk) {
+      const int ce = min(hi, cb + kSlotChunk);
+      // stage the chunk's row addresses (batches of 8 slot loads per thread in
+      // flight at once), plus kTile zero-row entries past its end
+      bool lane_bad = false;
+      for (int i0 = 0; i0 < ce - cb + kTile; i0 += 8 * kBatch) {
+        int v[8];
+        const bool early = hint_ok && cb == lo && i0 == 0;
 #pragma unroll
-      for (int k = 2; k < kPfAhead; ++k)
-        if (cb + k * kTile < ce) prefetch_tile(sink_lds, wave, pf_plan, rows_lds, k * kTile);
-    }
-    int buf = 0;
-    for (int t0 = cb; t0 < ce; t0 += kTile) {
-      // Waiting for this wave's gathers of tile t0: the prefetches issued
-      // after them only add to the loads still allowed in flight.
-      if (t0 + kTile < ce) wait_vmcnt<kWaitAhead>();
-      else wait_vmcnt<0>();
-      lds_barrier();  // tile t0 is in LDS for every wave; the buffer of tile t0 - 32 is free
-      if (t0 + 2 * kTile < ce) {
-        const int nb = buf == 0 ? kStages - 1 : buf - 1;
-        gather_tile<NW>(kv_lds + nb * kBufElems * 2, wave, gp, rows_lds, t0 + 2 * kTile - cb);
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kBatch + tid;
+          v[u] = i < ce - cb ? (early ? v_h[u] : slot_row[cb + i]) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kBatch + tid;
+          const bool ok = (uint32_t)v[u] < pool_lim;
+          lane_bad |= (i < ce - cb) && !ok;
+          if (i < ce - cb + kTile) rows_lds[i] = ok ? pool + (size_t)(uint32_t)v[u] * (kDk * 2) : zero_row;
+        }
       }
-      // (the staged rows of the chunk reach kTile entries past its end, so a
-      // prefetched tile that starts inside the chunk stays in range)
-      if (pf_on && t0 + kPfAhead * kTile < ce)
-        prefetch_tile(sink_lds, wave, pf_plan, rows_lds, t0 + kPfAhead * kTile - cb);
-      compute_tile(kv + buf * kBufElems, t0, cb, ce, chunk_bad);
-      ++seq;
-      buf = buf + 1 == kStages ? 0 : buf + 1;
+      bad_slot |= lane_bad;
+      // Drain every load the compiler issued (the query loads too): it cannot
+      // see the gathers below, and with any of its own loads still pending it
+      // puts vmcnt waits before the score MFMAs of every tile, which then also
+      // wait for the gathers of the next tiles and undo the lookahead.
+      wait_vmcnt<0>();
+      // Row addresses visible to every wave, and whether any slot was invalid.
+      // No gather is in flight here (the previous chunk ended with a full
+      // drain), so the full barrier costs nothing.
+      const bool chunk_bad = __syncthreads_or(lane_bad) != 0;
+      const uint32_t kv_lds = lds_addr_of(kv);
+      const uint32_t sink_lds = lds_addr_of(pf_sink);
+      if constexpr (kGather) {
+        gather_tile<NGW>(kv_lds, gw, gp, rows_lds, 0);
+        if (cb + kTile < ce) gather_tile<NGW>(kv_lds + kBufElems * 2, gw, gp, rows_lds, kTile);
+        // tiles 2 .. kPfAhead - 1 of the chunk, before the loop prefetches the rest
+        if (pf_on) {
+#pragma unroll
+          for (int k = 2; k < kPfAhead; ++k)
+            if (cb + k * kTile < ce) prefetch(sink_lds, k * kTile);
+        }
+      }
+      int buf = 0;
+      for (int t0 = cb; t0 < ce; t0 += kTile) {
+        // Waiting for this wave's gathers of tile t0: the prefetches issued
+        // after them only add to the loads still allowed in flight.
+        if constexpr (kGather) {
+          if (t0 + kTile < ce) wait_vmcnt<kWaitAhead>();
+          else wait_vmcnt<0>();
+        }
+        lds_barrier();  // tile t0 is in LDS for every wave; the buffer of tile t0 - 32 is free
+        if constexpr (kGather) {
+          if (t0 + 2 * kTile < ce) {
+            const int nb = buf == 0 ? kStages - 1 : buf - 1;
+            gather_tile<NGW>(kv_lds + nb * kBufElems * 2, gw, gp, rows_lds, t0 + 2 * kTile - cb);
+          }
+          // (the staged rows of the chunk reach kTile entries past its end, so a
+          // prefetched tile that starts inside the chunk stays in range)
+          if (pf_on && t0 + kPfAhead * kTile < ce) prefetch(sink_lds, t0 + kPfAhead * kTile - cb);
+        }
+        if constexpr (kCompute) {
+          compute_tile(kv + buf * kBufElems, t0, cb, ce, chunk_bad);
+          ++seq;
+        }
+        buf = buf + 1 == kStages ? 0 : buf + 1;
+      }
+      lds_barrier();  // every wave is done with the tiles and the slot chunk
     }
-    lds_barrier();  // every wave is done with the tiles and the slot chunk
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  if constexpr (NG == 0) {
+    main_loop(yes{}, yes{});
+  } else {
+    if (gather_only) {
+      // (returning here keeps the pairs' query registers and accumulators
+      // out of this path's live ranges)
+      main_loop(yes{}, no{});
+      if (bad_slot) flag_error(a.err, MLA_DEVERR_SLOT_RANGE);
+      return;
+    }
+    main_loop(no{}, yes{});
   }
   if (bad_slot) flag_error(a.err, MLA_DEVERR_SLOT_RANGE);
 
@@ -391,9 +451,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_bf16_kernel(Args a) {
 template <int NB, bool kPf>
 hipError_t launch_nb_pf(const Args& b, long units, hipStream_t stream) {
   if (b.balance_units > 0)
-    hipLaunchKernelGGL((split_bf16_kernel<NB, true, kPf>), dim3(xcd_grid(units, b.xcd_chunk)), dim3(NB * 128), 0, stream, b);
+    hipLaunchKernelGGL((split_bf16_kernel<NB, true, kPf>), dim3(xcd_grid(units, b.xcd_chunk)), dim3(kThreads<NB>), 0, stream, b);
   else
-    hipLaunchKernelGGL((split_bf16_kernel<NB, false, kPf>), dim3(xcd_grid(units, b.xcd_chunk)), dim3(NB * 128), 0, stream, b);
+    hipLaunchKernelGGL((split_bf16_kernel<NB, false, kPf>), dim3(xcd_grid(units, b.xcd_chunk)), dim3(kThreads<NB>), 0, stream, b);
   return hipGetLastError();
 }
 
