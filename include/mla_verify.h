@@ -136,7 +136,9 @@ typedef struct mla_mask_t {
 /* Plan of one call, as chosen by the library (for tests and measurement). */
 typedef struct mla_plan_t {
   int nsplit;            /* KV splits per sequence actually used */
-  int waves_per_group;   /* wavefronts per workgroup (two per 16-row query block) */
+  int waves_per_group;   /* wavefronts per workgroup: two per 16-row query block,
+                            plus two that only gather when the bf16 kernel
+                            has an odd number of blocks */
   int row_groups;        /* workgroups along the query-row axis per split */
   int grid;              /* split-kernel workgroups with work (the launch adds
                             idle ones up to a multiple of 8, and up to whole

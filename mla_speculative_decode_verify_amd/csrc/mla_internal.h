@@ -16,6 +16,18 @@ constexpr int kDrope = 64;
 // each split's own length).
 constexpr int kPfMinTiles = 24;
 
+// Gather-only wavefronts of a bf16 split workgroup with `nb` 16-row blocks.
+// With an odd number of blocks the pairs leave SIMDs 2 and 3 one wavefront
+// short of SIMDs 0 and 1 (wavefront w runs on SIMD w % 4), and a SIMD's LDS
+// reads and MFMAs barely overlap, so the SIMDs holding three pairs' halves
+// set the tile time. Two extra wavefronts, which land on SIMDs 2 and 3, then
+// issue every gather and L2 prefetch (and read their row addresses from LDS)
+// in place of the pairs. MLA_GATHER_WAVES=0 builds the kernel without them.
+#ifndef MLA_GATHER_WAVES
+#define MLA_GATHER_WAVES 1
+#endif
+constexpr int bf16_gather_waves(int nb) { return (MLA_GATHER_WAVES && nb % 2 == 1) ? 2 : 0; }
+
 // Everything a kernel needs, with pointers already validated by the host.
 struct Args {
   const void* q;            // bf16 [batch, rows, 576]

@@ -13,6 +13,10 @@
 // accumulator, which leaves room for two or three wavefronts per SIMD: the
 // hardware hides LDS and MFMA latency by switching between them.
 //
+// With an odd number of blocks two more wavefronts, which run on SIMDs 2 and
+// 3 (the SIMDs the pairs leave one wavefront short), do nothing but issue
+// the gathers and L2 prefetches of step 1; otherwise the pairs issue them.
+//
 // Per tile of 32 cache positions:
 //   1. gather: 16-byte pieces of the 32 latent rows (each 1152 B row is 72
 //      pieces) are loaded through the slot table straight into an LDS tile
@@ -65,17 +69,8 @@ constexpr int kAhead = MLA_KAHEAD;                 // LDS fragments read ahead o
 #endif
 constexpr int kVAhead = MLA_VAHEAD;                // V fragments read ahead of their MFMAs
 
-// Gather-only wavefronts per workgroup. With an odd number of blocks the
-// pairs leave SIMDs 2 and 3 one wavefront short of SIMDs 0 and 1 (wavefront w
-// runs on SIMD w % 4), and a SIMD's LDS reads and MFMAs barely overlap, so
-// the SIMDs that hold three pairs' halves set the tile time. Two extra
-// wavefronts, which land on SIMDs 2 and 3, then issue every gather and L2
-// prefetch (and read their row addresses from LDS) in place of the pairs.
-#ifndef MLA_GATHER_WAVES
-#define MLA_GATHER_WAVES 1
-#endif
 template <int NB>
-constexpr int kGatherWaves = (MLA_GATHER_WAVES && NB % 2 == 1) ? 2 : 0;
+constexpr int kGatherWaves = bf16_gather_waves(NB);
 template <int NB>
 constexpr int kThreads = (2 * NB + kGatherWaves<NB>) * 64;
 

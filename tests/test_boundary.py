@@ -174,13 +174,14 @@ def test_choose_nsplit_rules(L):
 
 
 def test_plan_shapes(L):
-    # 72 rows: 5 blocks of 16, two wavefronts each; with 64 splits three
-    # groups of 2 blocks (the last one half empty) fit one pass of the grid
+    # 72 rows: 5 blocks of 16, two wavefronts each (plus two gather-only
+    # wavefronts for an odd block count); with 64 splits three groups of 2
+    # blocks (the last one half empty) fit one pass of the grid
     p = B.plan(1, 9, 8, 16393, nsplit=64)
     assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (64, 4, 3, 192, 2)
     assert p["workspace_bytes"] == 64 * 72 * 1036 + 4
     p = B.plan(1, 9, 8, 16393, nsplit=200)
-    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (200, 10, 1, 200, 5)
+    assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (200, 12, 1, 200, 5)
     p = B.plan(1, 9, 64, 4105, nsplit=16)
     assert (p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (8, 9, 144, 4)
     # 144 rows = 9 blocks: one pass of the grid either way, so 3 groups of 4
@@ -188,7 +189,7 @@ def test_plan_shapes(L):
     p = B.plan(1, 9, 16, 4105, nsplit=16)
     assert (p["waves_per_group"], p["row_groups"], p["row_blocks"]) == (8, 3, 4)
     p = B.plan(2, 1, 1, 10, nsplit=1)
-    assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 2
+    assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 4
 
 
 def test_plan_balanced_splits(L):
@@ -301,7 +302,7 @@ def test_plan_invariants_over_shapes(L):
                 assert 1 <= p["row_blocks"] <= 6
                 assert p["row_groups"] * p["row_blocks"] >= blocks
                 assert (p["row_groups"] - 1) * p["row_blocks"] < blocks
-                assert p["waves_per_group"] == 2 * p["row_blocks"]
+                assert p["waves_per_group"] == 2 * p["row_blocks"] + (2 if p["row_blocks"] % 2 else 0)
                 tiles = -(-n // 32)
                 if p["balanced"]:
                     assert p["grid"] <= 256
