@@ -227,20 +227,22 @@ struct Layout {
 // groups gathering every key once each (the second read mostly from L2).
 // Each layout's split + merge kernel time was fitted to batch-1 calls at
 // prefixes 256 to 64k (least squares over 16 to 23 points each, rms error
-// 0.3-0.6 us) as
+// 0.25-0.7 us) as
 //   f + t * T + p * R * S / 1000 + q * G * S * T / 1000
 // with T the tiles of the longest split, R the rows, S the splits and G the
 // groups (the last term: HBM traffic growing with the workgroups in
-// flight). Smaller groups win up to about 32k positions (one tile of 6
-// wavefronts takes 1.55 us where one of 10 takes 1.9, and fewer splits mean
-// fewer partials), one group of 5 beyond (measured: 37.5 us at 64k against
-// 41.4 for 2 x 3 blocks).
+// flight; with one group S * T is about the tile count, so that fit leaves
+// it out). The 5- and 3-block workgroups carry two gather-only wavefronts.
+// Smaller groups win up to about 32k positions (fewer wavefronts per SIMD
+// make a tile cheaper, and fewer splits mean fewer partials), one group of
+// 5 beyond (measured: 35.5 us of kernel time at 64k against 37.0 for
+// 2 x 3 blocks).
 struct FiveBlockFit {
   int nb;
   double f, t, p, q;
 };
 constexpr FiveBlockFit kFiveBlockFits[3] = {
-    {5, 13.387, 1.536, 0.510, 0.897}, {3, 12.074, 1.547, 0.302, 0.070}, {2, 12.100, 1.355, 0.137, 0.980}};
+    {5, 14.025, 1.379, 0.516, 0.0}, {3, 12.831, 1.222, 0.282, 0.183}, {2, 11.968, 1.454, 0.097, 0.771}};
 constexpr double kMergeKernelUs = 4.5;  // what a single split saves: no merge kernel
 
 double five_block_cost_us(const FiveBlockFit& fit, int groups, long tiles, long s, long rows) {
@@ -256,6 +258,9 @@ Layout plan_five_blocks(int rows, long tiles, int num_cus, int nsplit) {
   double best = 0.0;
   bool have = false;
   for (const FiveBlockFit& fit : kFiveBlockFits) {
+#ifdef MLA_FIVE_BLOCK_NB
+    if (fit.nb != MLA_FIVE_BLOCK_NB) continue;  // tuning builds that time one layout
+#endif
     const int groups = (5 + fit.nb - 1) / fit.nb;
     const long one_pass = std::max<long>(1, num_cus / groups);
     long lo = 1, hi = std::min(one_pass, tiles);
@@ -316,6 +321,9 @@ Layout plan_layout(int batch, int q_len, int heads, int keys, int kv_dtype, int 
   for (int nb = 1; nb <= kMaxBlocks; ++nb) {
     // one workgroup when the blocks fit; otherwise 4 to 6 blocks per group
     if (blocks <= kMaxBlocks ? nb != blocks : nb < 4) continue;
+#ifdef MLA_ONLY_NB
+    if (blocks > kMaxBlocks && nb != MLA_ONLY_NB) continue;  // tuning builds that time one group size
+#endif
     const int groups = (blocks + nb - 1) / nb;
     const long wgs = (long)batch * groups;
     double cost = 0.0;
