@@ -64,6 +64,16 @@ def test_h64_prefix_64k_all_heads():
     _check(w, [0, 16])
 
 
+def test_five_block_groups_with_prefetch():
+    # H=64 at 32k with 32 splits: 8 row groups of 5 blocks, each with the two
+    # gather-only wavefronts, and splits of 33 tiles, long enough for the L2
+    # prefetch (the only layout that runs both)
+    w = I.make_verify("h64_32k_random", batch=1, q_len=9, heads=64, prefixes=[32768], seed=65, layout="random")
+    p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=32)
+    assert (p["row_blocks"], p["row_groups"], p["l2_prefetch"]) == (5, 8, 1)
+    _check(w, [32])
+
+
 def test_c4_tree_ragged_all_heads():
     w = I.workload("c4")
     _check(w, [0, 8])
