@@ -74,6 +74,24 @@ def test_five_block_groups_with_prefetch():
     _check(w, [32])
 
 
+@pytest.mark.parametrize("name,batch,q_len,heads,prefixes,nsplits,blocks,balanced,prefetch", [
+    ("gw_nb1_prefetch", 1, 1, 8, [20000], [8], 1, 0, 1),     # one block, long splits: L2 prefetch
+    ("gw_nb1_ragged", 3, 1, 8, [9000, 300, 5000], [0], 1, 1, 0),
+    ("gw_nb3_ragged", 3, 9, 4, [9000, 300, 5000], [0], 3, 1, 0),
+    ("gw_nb3_prefetch", 3, 9, 4, [9000, 300, 5000], [4], 3, 0, 1),
+])
+def test_gather_wave_layouts(name, batch, q_len, heads, prefixes, nsplits, blocks, balanced, prefetch):
+    # the other odd block counts that run the two gather-only wavefronts,
+    # with uniform and length-following split counts and with the L2 prefetch
+    w = I.make_verify(name, batch=batch, q_len=q_len, heads=heads, prefixes=prefixes, seed=66 + batch + heads,
+                      layout="random", mask="tree" if q_len > 1 else "causal")
+    p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=nsplits[0],
+               mask="tree" if q_len > 1 else "causal")
+    assert (p["row_blocks"], p["balanced"], p["l2_prefetch"], p["waves_per_group"]) == \
+        (blocks, balanced, prefetch, 2 * blocks + 2)
+    _check(w, nsplits)
+
+
 def test_c4_tree_ragged_all_heads():
     w = I.workload("c4")
     _check(w, [0, 8])
