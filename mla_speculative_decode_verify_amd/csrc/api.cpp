@@ -182,8 +182,13 @@ int release_workspace(int dev, hipStream_t stream) {
 // (11.4 us with 6 blocks: more query rows to load and partial rows to
 // store per workgroup); with several splits the merge kernel adds about
 // 4 us, and every split's partials (1036 bytes per query row, written and
-// read back) about 0.49 us per MB.
-constexpr double kTileUs[7] = {0.0, 1.86, 1.86, 1.86, 1.86, 1.86, 2.21};  // by blocks per workgroup
+// read back) about 0.49 us per MB. With 4 blocks the workgroup carries four
+// gather-only wavefronts (one per SIMD), which made its tile cheaper: 1.60 us
+// here. (Least squares over its H=64 calls at full occupancy, the other
+// constants kept, gives 1.52 us, but then 64k prefixes would take 4 blocks,
+// which measured 2-3% slower there than 6; 1.60 keeps the measured order at
+// 16k and 32k, where 4 blocks are fastest, and at 64k.)
+constexpr double kTileUs[7] = {0.0, 1.86, 1.86, 1.86, 1.60, 1.86, 2.21};  // by blocks per workgroup
 constexpr double kFixedUs[7] = {0.0, 8.1, 8.1, 8.1, 8.1, 8.1, 11.4};
 constexpr double kPartUsPerByte = 0.49e-6;
 constexpr double kMergeUs = 4.0;

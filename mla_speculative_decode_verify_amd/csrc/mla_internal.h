@@ -26,7 +26,12 @@ constexpr int kPfMinTiles = 24;
 #ifndef MLA_GATHER_WAVES
 #define MLA_GATHER_WAVES 1
 #endif
-constexpr int bf16_gather_waves(int nb) { return (MLA_GATHER_WAVES && nb % 2 == 1) ? 2 : 0; }
+#ifndef MLA_GATHER_WAVES_EVEN
+#define MLA_GATHER_WAVES_EVEN 1
+#endif
+constexpr int bf16_gather_waves(int nb) {
+  return !MLA_GATHER_WAVES ? 0 : nb % 2 == 1 ? 2 : (MLA_GATHER_WAVES_EVEN && (nb == 2 || nb == 4)) ? 4 : 0;
+}
 
 // Everything a kernel needs, with pointers already validated by the host.
 struct Args {

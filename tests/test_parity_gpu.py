@@ -79,16 +79,21 @@ def test_five_block_groups_with_prefetch():
     ("gw_nb1_ragged", 3, 1, 8, [9000, 300, 5000], [0], 1, 1, 0),
     ("gw_nb3_ragged", 3, 9, 4, [9000, 300, 5000], [0], 3, 1, 0),
     ("gw_nb3_prefetch", 3, 9, 4, [9000, 300, 5000], [4], 3, 0, 1),
+    ("gw_nb2_ragged", 3, 9, 3, [9000, 300, 5000], [0], 2, 1, 0),
+    ("gw_nb2_prefetch", 1, 9, 3, [20000], [8], 2, 0, 1),
+    ("gw_nb4_ragged", 2, 8, 8, [9000, 5000], [0], 4, 1, 0),
+    ("gw_nb4_prefetch", 2, 8, 8, [9000, 5000], [4], 4, 0, 1),
 ])
 def test_gather_wave_layouts(name, batch, q_len, heads, prefixes, nsplits, blocks, balanced, prefetch):
-    # the other odd block counts that run the two gather-only wavefronts,
-    # with uniform and length-following split counts and with the L2 prefetch
+    # block counts that run gather-only wavefronts (two for 1, 3 and 5 blocks,
+    # four for 2 and 4) besides the headline shapes, with uniform and
+    # length-following split counts and with the L2 prefetch
     w = I.make_verify(name, batch=batch, q_len=q_len, heads=heads, prefixes=prefixes, seed=66 + batch + heads,
                       layout="random", mask="tree" if q_len > 1 else "causal")
     p = B.plan(w.batch, w.q_len, w.heads, w.slot_stride, nsplit=nsplits[0],
                mask="tree" if q_len > 1 else "causal")
     assert (p["row_blocks"], p["balanced"], p["l2_prefetch"], p["waves_per_group"]) == \
-        (blocks, balanced, prefetch, 2 * blocks + 2)
+        (blocks, balanced, prefetch, 2 * blocks + (2 if blocks % 2 else 4))
     _check(w, nsplits)
 
 
@@ -221,8 +226,9 @@ def test_mixed_plans_share_the_workspace():
     # Calls with different plans run back to back on one stream and share the
     # library's workspace: uniform splits with two groups of 3 blocks (H=8 at
     # 9k) and with one 5-block group (H=8 at 60k), length-following splits
-    # with 6-block groups and the L2 prefetch (ragged tree batch, H=64), 8
-    # groups of 5 blocks (H=64), and the fp8 sparse path.
+    # with 6-block groups and the L2 prefetch (ragged tree batch, H=64), 9
+    # groups of 4 blocks with four gather-only wavefronts each (H=64), and the
+    # fp8 sparse path.
     # Each result must equal, bit for bit, the same call made first on its
     # own, whatever ran between (stale split counts or partials would show).
     import numpy as np
@@ -244,7 +250,7 @@ def test_mixed_plans_share_the_workspace():
     plans = [B.plan(w.batch, w.q_len, w.heads, w.slot_stride, mask=w.mask) for w in shapes[:3] + shapes[4:]]
     assert plans[0]["row_blocks"] == 3 and plans[0]["row_groups"] == 2 and plans[0]["balanced"] == 0
     assert plans[1]["balanced"] == 1 and plans[1]["row_blocks"] == 6 and plans[1]["l2_prefetch"] == 1
-    assert plans[2]["row_blocks"] == 5 and plans[2]["row_groups"] == 8
+    assert plans[2]["row_blocks"] == 4 and plans[2]["row_groups"] == 9 and plans[2]["waves_per_group"] == 12
     assert plans[3]["row_blocks"] == 5 and plans[3]["row_groups"] == 1
     order = [1, 0, 4, 3, 2, 1, 3, 0, 4, 2, 1]
     for k in order:
