@@ -137,8 +137,8 @@ typedef struct mla_mask_t {
 typedef struct mla_plan_t {
   int nsplit;            /* KV splits per sequence actually used */
   int waves_per_group;   /* wavefronts per workgroup: two per 16-row query block,
-                            plus two that only gather when the bf16 kernel
-                            has an odd number of blocks */
+                            plus the bf16 kernel's gather-only ones (two with
+                            1, 3 or 5 blocks, four with 2 or 4) */
   int row_groups;        /* workgroups along the query-row axis per split */
   int grid;              /* split-kernel workgroups with work (the launch adds
                             idle ones up to a multiple of 8, and up to whole

@@ -17,12 +17,16 @@ constexpr int kDrope = 64;
 constexpr int kPfMinTiles = 24;
 
 // Gather-only wavefronts of a bf16 split workgroup with `nb` 16-row blocks.
-// With an odd number of blocks the pairs leave SIMDs 2 and 3 one wavefront
-// short of SIMDs 0 and 1 (wavefront w runs on SIMD w % 4), and a SIMD's LDS
-// reads and MFMAs barely overlap, so the SIMDs holding three pairs' halves
-// set the tile time. Two extra wavefronts, which land on SIMDs 2 and 3, then
-// issue every gather and L2 prefetch (and read their row addresses from LDS)
-// in place of the pairs. MLA_GATHER_WAVES=0 builds the kernel without them.
+// They issue every gather and L2 prefetch (and read the row addresses from
+// LDS) in place of the pairs, which then run no global-memory instruction
+// in the tile loop. With an odd number of blocks the pairs leave SIMDs 2 and
+// 3 one wavefront short of SIMDs 0 and 1 (wavefront w runs on SIMD w % 4),
+// and a SIMD's LDS reads and MFMAs barely overlap, so two extra wavefronts
+// land on SIMDs 2 and 3 and also even out the SIMDs. With 2 or 4 blocks four
+// extra wavefronts take one SIMD each. With 6 blocks three pair halves per
+// SIMD leave no registers for a fourth wavefront. MLA_GATHER_WAVES=0 (or
+// MLA_GATHER_WAVES_EVEN=0 for the even counts) builds the kernel without
+// them.
 #ifndef MLA_GATHER_WAVES
 #define MLA_GATHER_WAVES 1
 #endif

@@ -13,9 +13,10 @@
 // accumulator, which leaves room for two or three wavefronts per SIMD: the
 // hardware hides LDS and MFMA latency by switching between them.
 //
-// With an odd number of blocks two more wavefronts, which run on SIMDs 2 and
-// 3 (the SIMDs the pairs leave one wavefront short), do nothing but issue
-// the gathers and L2 prefetches of step 1; otherwise the pairs issue them.
+// Up to 4 blocks, and with 5, extra wavefronts do nothing but issue the
+// gathers and L2 prefetches of step 1: two on SIMDs 2 and 3 (the SIMDs the
+// pairs leave one wavefront short) for an odd number of blocks, one per SIMD
+// for 2 and 4. With 6 blocks the pairs issue them.
 //
 // Per tile of 32 cache positions:
 //   1. gather: 16-byte pieces of the 32 latent rows (each 1152 B row is 72
