@@ -561,7 +561,7 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
   Call c;
   if ((st = make_plan(q, kv_cache, mask_desc, nsplit, cus, &c)) != MLA_OK) return st;
   plan->nsplit = c.a.nsplit;
-  plan->waves_per_group = 2 * c.nb + (c.kernel == 0 ? mla::bf16_gather_waves(c.nb) : 0);
+  plan->waves_per_group = 2 * c.nb + (c.kernel == 0 ? mla::bf16_gather_waves(c.nb) : mla::fp8_load_waves(c.nb));
   plan->row_groups = c.groups;
   plan->grid = c.a.balance_units > 0 ? c.a.balance_units * c.groups
                                       : c.a.nsplit * c.groups * q->batch * (c.kernel == 1 ? q->q_len : 1);

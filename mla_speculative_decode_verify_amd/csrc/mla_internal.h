@@ -37,6 +37,15 @@ constexpr int bf16_gather_waves(int nb) {
   return !MLA_GATHER_WAVES ? 0 : nb % 2 == 1 ? 2 : (MLA_GATHER_WAVES_EVEN && (nb == 2 || nb == 4)) ? 4 : 0;
 }
 
+// Load-only wavefronts of an fp8 split workgroup: they stage the positions
+// and slots, load each tile's fp8 rows, convert them to bf16 and write the
+// LDS tile, one wavefront per SIMD, so the pairs only compute.
+// MLA_FP8_LOAD_WAVES=0 builds the kernel with the pairs loading the tiles.
+#ifndef MLA_FP8_LOAD_WAVES
+#define MLA_FP8_LOAD_WAVES 4
+#endif
+constexpr int fp8_load_waves(int) { return MLA_FP8_LOAD_WAVES; }
+
 // Everything a kernel needs, with pointers already validated by the host.
 struct Args {
   const void* q;            // bf16 [batch, rows, 576]

@@ -11,10 +11,11 @@
 // The compute follows the bf16 verify kernel (pairs of wavefronts per 16-row
 // block, each half owning 9 k-steps of the score and 256 output columns),
 // with three differences:
-//   * Tiles are built by the wavefronts themselves: 8-byte fp8 pieces are
-//     loaded into registers one tile ahead, converted exactly to bf16 (every
-//     E4M3FN value is a bf16 value) and written to a padded LDS tile of the
-//     same [32][576 + 16] layout; rope pieces are copied as they are.
+//   * Tiles are built by four load-only wavefronts (one per SIMD), so the
+//     pairs only compute: 8-byte fp8 pieces are loaded into registers one
+//     tile ahead, converted exactly to bf16 (every E4M3FN value is a bf16
+//     value) and written to a padded LDS tile of the same [32][576 + 16]
+//     layout; rope pieces are copied as they are.
 //   * The per-token scale stays in fp32: the score is
 //       s_j = scale_j * <q_lat, lat_j> + <q_rope, rope_j>
 //     from separate latent and rope MFMA accumulators, and the weight that
@@ -25,6 +26,8 @@
 //   * Keys that are past the split end, or whose position or slot is out of
 //     range, get an additive score bias of -inf (and read the zero row), so
 //     they carry no weight; no draft mask exists on this path.
+#include <type_traits>
+
 #include "device_common.h"
 #include "mla_internal.h"
 #include "mla_verify.h"
@@ -151,9 +154,14 @@ __device__ __forceinline__ void store_tile(const TileRegs<NW>& R, int tid, __bf1
 }
 
 template <int NB>
-__global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
-  constexpr int NW = 2 * NB;
-  constexpr int kNT = NW * 64;
+constexpr int kThreads8 = (2 * NB + fp8_load_waves(NB)) * 64;
+
+template <int NB>
+__global__ __launch_bounds__(kThreads8<NB>, 1) void split_fp8_topk_kernel(Args a) {
+  constexpr int NW = 2 * NB;                 // compute wavefronts (a pair per block)
+  constexpr int NL = fp8_load_waves(NB);     // load-only wavefronts after them
+  constexpr int NLW = NL > 0 ? NL : NW;      // wavefronts that load the tiles
+  constexpr int kNT = (NW + NL) * 64;        // threads that stage the chunk
   __shared__ __attribute__((aligned(16))) __bf16 kv[2 * kTileElems];   // double-buffered tile
   __shared__ __attribute__((aligned(16))) float sc_lds[2][3][kTile];   // scale, 1/scale, bias per key
   __shared__ __attribute__((aligned(16))) f32x4 spart[NW][2][64];      // partial scores per wave
@@ -161,8 +169,9 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
   __shared__ int pair_seq[NW];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
+  const bool loader = NL > 0 && wave >= NW;  // wave-uniform
   const int half = wave & 1, blk = wave >> 1;
   // unit = (z * nsplit + split) * row_groups + grp with z = b * q_len + qi,
   // in XCD-aware order
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
   const int r_glob = qi * H + min(h, H - 1);  // row within the sequence: query * heads + head
 
   bf16x8 qr[kHalfSteps];
-  {
+  if (!loader) {
     const __bf16* qp =
         static_cast<const __bf16*>(a.q) + ((size_t)b * R + r_glob) * kDk + 32 * kHalfSteps * half + 8 * g;
 #pragma unroll
@@ -218,7 +227,7 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
   const int offA = li * kLdsStride + 32 * kHalfSteps * half + 8 * g;
   const int offV = (4 * g + (li >> 2)) * kLdsStride + 256 * half + 4 * (li & 3);
 
-  if (lane == 0) __hip_atomic_store(&pair_seq[wave], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (lane == 0 && !loader) __hip_atomic_store(&pair_seq[wave], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   int seq = 0;
 
   auto compute_tile = [&](const __bf16* cur, const float* sc, const float* isc, const float* bias) {
@@ -326,52 +335,83 @@ __global__ __launch_bounds__(NB * 128, 1) void split_fp8_topk_kernel(Args a) {
     }
   };
 
-  TileRegs<NW> regs;
-  for (int cb = lo; cb < hi; cb += kChunk) {
-    const int ce = min(hi, cb + kChunk);
-    // ---- stage the chunk: top-k position -> checked position -> checked pool row
-    for (int i0 = 0; i0 < ce - cb; i0 += 8 * kNT) {
-      int p[8], sl[8];
+  // ---- main loop. kLoad / kCompute select a wavefront's roles: with
+  // load-only wavefronts (NL > 0) those stage nothing more than the others but
+  // load, convert and store every tile, and the pairs only compute;
+  // otherwise every wavefront does both. Both roles meet at the same
+  // barriers: two per chunk before its first tile, one per tile.
+  auto main_loop = [&](auto load_role, auto compute_role) {
+    constexpr bool kLoad = decltype(load_role)::value;
+    constexpr bool kCompute = decltype(compute_role)::value;
+    const int ltid = NL > 0 ? tid - NW * 64 : tid;  // thread index among the loading wavefronts
+    TileRegs<NLW> regs;
+    for (int cb = lo; cb < hi; cb += kChunk) {
+      const int ce = min(hi, cb + kChunk);
+      // ---- stage the chunk: top-k position -> checked position -> checked pool row
+      for (int i0 = 0; i0 < ce - cb; i0 += 8 * kNT) {
+        int p[8], sl[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kNT + tid;
-        p[u] = i < ce - cb ? topk_row[cb + i] : 0;
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kNT + tid;
+          p[u] = i < ce - cb ? topk_row[cb + i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kNT + tid;
+          const bool pos_ok = (uint32_t)p[u] < (uint32_t)n;
+          bad_pos |= (i < ce - cb) && !pos_ok;
+          sl[u] = (i < ce - cb && pos_ok) ? slot_row[p[u]] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kNT + tid;
+          const bool slot_ok = (uint32_t)sl[u] < pool_lim;
+          bad_slot |= sl[u] != -1 && !slot_ok;
+          if (i < ce - cb) slots_lds[i] = slot_ok ? sl[u] : -1;
+        }
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kNT + tid;
-        const bool pos_ok = (uint32_t)p[u] < (uint32_t)n;
-        bad_pos |= (i < ce - cb) && !pos_ok;
-        sl[u] = (i < ce - cb && pos_ok) ? slot_row[p[u]] : -1;
+      lds_barrier();  // staged rows visible to every wave
+      if constexpr (kLoad) {
+        load_tile<NLW>(regs, ltid, slots_lds, cb, cb, ce, lat, rope, a.kscale, zero_row);
+        store_tile<NLW>(regs, ltid, kv, sc_lds[0][0], sc_lds[0][1], sc_lds[0][2]);
+        if (cb + kTile < ce) load_tile<NLW>(regs, ltid, slots_lds, cb, cb + kTile, ce, lat, rope, a.kscale, zero_row);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kNT + tid;
-        const bool slot_ok = (uint32_t)sl[u] < pool_lim;
-        bad_slot |= sl[u] != -1 && !slot_ok;
-        if (i < ce - cb) slots_lds[i] = slot_ok ? sl[u] : -1;
+      lds_barrier();
+      int buf = 0;
+      for (int t0 = cb; t0 < ce; t0 += kTile) {
+        if constexpr (kCompute) {
+          compute_tile(kv + buf * kTileElems, sc_lds[buf][0], sc_lds[buf][1], sc_lds[buf][2]);
+          ++seq;
+        }
+        if constexpr (kLoad) {
+          if (t0 + kTile < ce) {
+            // The other buffer was last read in the previous tile, which every
+            // wave finished before the barrier that ended it.
+            store_tile<NLW>(regs, ltid, kv + (buf ^ 1) * kTileElems, sc_lds[buf ^ 1][0], sc_lds[buf ^ 1][1],
+                            sc_lds[buf ^ 1][2]);
+            if (t0 + 2 * kTile < ce)
+              load_tile<NLW>(regs, ltid, slots_lds, cb, t0 + 2 * kTile, ce, lat, rope, a.kscale, zero_row);
+          }
+        }
+        lds_barrier();  // next tile in LDS; this tile's buffer and the partial scores are free
+        buf ^= 1;
       }
     }
-    lds_barrier();  // staged rows visible to every wave
-    load_tile<NW>(regs, tid, slots_lds, cb, cb, ce, lat, rope, a.kscale, zero_row);
-    store_tile<NW>(regs, tid, kv, sc_lds[0][0], sc_lds[0][1], sc_lds[0][2]);
-    if (cb + kTile < ce) load_tile<NW>(regs, tid, slots_lds, cb, cb + kTile, ce, lat, rope, a.kscale, zero_row);
-    lds_barrier();
-    int buf = 0;
-    for (int t0 = cb; t0 < ce; t0 += kTile) {
-      compute_tile(kv + buf * kTileElems, sc_lds[buf][0], sc_lds[buf][1], sc_lds[buf][2]);
-      ++seq;
-      if (t0 + kTile < ce) {
-        // The other buffer was last read in the previous tile, which every
-        // wave finished before the barrier that ended it.
-        store_tile<NW>(regs, tid, kv + (buf ^ 1) * kTileElems, sc_lds[buf ^ 1][0], sc_lds[buf ^ 1][1],
-                       sc_lds[buf ^ 1][2]);
-        if (t0 + 2 * kTile < ce)
-          load_tile<NW>(regs, tid, slots_lds, cb, t0 + 2 * kTile, ce, lat, rope, a.kscale, zero_row);
-      }
-      lds_barrier();  // next tile in LDS; this tile's buffer and the partial scores are free
-      buf ^= 1;
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  if constexpr (NL == 0) {
+    main_loop(yes{}, yes{});
+  } else {
+    if (loader) {
+      // (returning here keeps the pairs' query registers and accumulators
+      // out of this path's live ranges)
+      main_loop(yes{}, no{});
+      if (__any(bad_pos) && lane == 0) flag_error(a.err, MLA_DEVERR_TOPK_RANGE);
+      if (__any(bad_slot) && lane == 0) flag_error(a.err, MLA_DEVERR_SLOT_RANGE);
+      return;
     }
+    main_loop(no{}, yes{});
   }
   if (__any(bad_pos) && lane == 0) flag_error(a.err, MLA_DEVERR_TOPK_RANGE);
   if (__any(bad_slot) && lane == 0) flag_error(a.err, MLA_DEVERR_SLOT_RANGE);
@@ -393,7 +433,8 @@ hipError_t launch_nb(const Args& a, int row_groups, hipStream_t stream) {
   Args b = a;
   b.row_groups = row_groups;
   const long units = (long)a.batch * a.q_len * a.nsplit * row_groups;
-  hipLaunchKernelGGL(split_fp8_topk_kernel<NB>, dim3(xcd_grid(units, b.xcd_chunk)), dim3(NB * 128), 0, stream, b);
+  hipLaunchKernelGGL(split_fp8_topk_kernel<NB>, dim3(xcd_grid(units, b.xcd_chunk)), dim3(kThreads8<NB>), 0, stream,
+                     b);
   return hipGetLastError();
 }
 

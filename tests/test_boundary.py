@@ -225,8 +225,8 @@ def test_plan_shapes_fp8_topk(L):
     assert p["workspace_bytes"] == 32 * 8 * 64 * 1036 + 32 * 4
     p = B.plan(2, 3, 80, 5000, nsplit=2, **fp8)       # 5 blocks -> groups of at most 4; grid over (seq, query)
     assert (p["row_blocks"], p["row_groups"], p["grid"]) == (4, 2, 2 * 2 * 2 * 3)
-    p = B.plan(1, 1, 8, 100, nsplit=1, **fp8)
-    assert (p["row_blocks"], p["waves_per_group"], p["workspace_bytes"]) == (1, 2, 0)
+    p = B.plan(1, 1, 8, 100, nsplit=1, **fp8)        # one block: a pair and four load-only wavefronts
+    assert (p["row_blocks"], p["waves_per_group"], p["workspace_bytes"]) == (1, 6, 0)
     # auto split count: key sets are (sequence, query) pairs; >= 128 list entries per split
     assert B.choose_nsplit(4, 3, 16, 512, kv_dtype=B.MLA_KV_FP8_E4M3) == 4
     assert B.choose_nsplit(1, 1, 64, 65536, kv_dtype=B.MLA_KV_FP8_E4M3) == 256
