@@ -64,6 +64,16 @@ def test_h64_prefix_64k_all_heads():
     _check(w, [0, 16])
 
 
+@pytest.mark.parametrize("name,nsplits", [
+    ("sweep_256", [1, 4, 0]),      # one tile per split at the library's count
+    ("sweep_1024", [8, 0]),
+    ("sweep_16384", [0, 64]),      # library: 9 row groups of 4 blocks, 27 splits; 64: 5-block groups, two passes
+])
+def test_h64_prefix_sweep_all_heads(name, nsplits):
+    # the other points of the pages' H=64 prefix sweep, over all 64 heads
+    _check(I.workload(name), nsplits)
+
+
 def test_five_block_groups_with_prefetch():
     # H=64 at 32k with 32 splits: 8 row groups of 5 blocks, each with the two
     # gather-only wavefronts, and splits of 33 tiles, long enough for the L2
