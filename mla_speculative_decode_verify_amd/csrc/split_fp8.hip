@@ -128,7 +128,7 @@ __device__ __forceinline__ void load_tile(TileRegs<NW>& R, int tid, const int* s
 // score bias (0 or -inf).
 template <int NW>
 __device__ __forceinline__ void store_tile(const TileRegs<NW>& R, int tid, __bf16* buf, float* sc, float* isc,
-                                           float* bias) {
+                                           float* bias, int* plain) {
   constexpr int kNT = TileRegs<NW>::kNT;
 #pragma unroll
   for (int u = 0; u < TileRegs<NW>::kL; ++u) {
@@ -150,6 +150,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<NW>& R, int tid, __bf1
     sc[tid] = R.scale;
     isc[tid] = (R.valid && R.scale != 0.f) ? 1.f / R.scale : 0.f;
     bias[tid] = R.valid ? 0.f : -INFINITY;
+    // plain tile: every key valid with a nonzero scale, so its bias is 0 and
+    // its reciprocal scale never needs the zero-scale fallback
+    const uint64_t ok = __ballot(R.valid && R.scale != 0.f);
+    if (tid == 0) *plain = (uint32_t)ok == 0xFFFFFFFFu ? 1 : 0;
   }
 }
 
@@ -164,6 +168,7 @@ __global__ __launch_bounds__(kThreads8<NB>, 1) void split_fp8_topk_kernel(Args a
   constexpr int kNT = (NW + NL) * 64;        // threads that stage the chunk
   __shared__ __attribute__((aligned(16))) __bf16 kv[2 * kTileElems];   // double-buffered tile
   __shared__ __attribute__((aligned(16))) float sc_lds[2][3][kTile];   // scale, 1/scale, bias per key
+  __shared__ int plain_lds[2];                                         // the tile's keys all plain (see store_tile)
   __shared__ __attribute__((aligned(16))) f32x4 spart[NW][2][64];      // partial scores per wave
   __shared__ int slots_lds[kChunk];                                    // pool row per entry, -1 = invalid
   __shared__ int pair_seq[NW];
@@ -230,8 +235,9 @@ __global__ __launch_bounds__(kThreads8<NB>, 1) void split_fp8_topk_kernel(Args a
   if (lane == 0 && !loader) __hip_atomic_store(&pair_seq[wave], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   int seq = 0;
 
-  auto compute_tile = [&](const __bf16* cur, const float* sc, const float* isc, const float* bias) {
+  auto compute_tile = [&](const __bf16* cur, const float* sc, const float* isc, const float* bias, bool plain_in) {
     if (!active) return;
+    const bool plain = __builtin_amdgcn_readfirstlane(plain_in ? 1 : 0) != 0;  // wave-uniform
     // ---- partial scores over this half's k-steps: latent and rope kept
     // apart. K fragments are read kAhead steps ahead of their MFMAs; the
     // scheduling barrier keeps the reads from sinking next to their use.
@@ -281,10 +287,12 @@ __global__ __launch_bounds__(kThreads8<NB>, 1) void split_fp8_topk_kernel(Args a
     asm volatile("" ::: "memory");
     // own + partner: addition commutes exactly, so both halves hold bitwise
     // the same sums
-    const f32x4 b0 = *reinterpret_cast<const f32x4*>(bias + 4 * g);
-    const f32x4 b1 = *reinterpret_cast<const f32x4*>(bias + 16 + 4 * g);
-    const f32x4 x0 = (own0 + spart[wave ^ 1][0][lane]) + b0;
-    const f32x4 x1 = (own1 + spart[wave ^ 1][1][lane]) + b1;
+    f32x4 x0 = own0 + spart[wave ^ 1][0][lane];
+    f32x4 x1 = own1 + spart[wave ^ 1][1][lane];
+    if (!plain) {  // some key of the tile is masked: add its -inf bias
+      x0 += *reinterpret_cast<const f32x4*>(bias + 4 * g);
+      x1 += *reinterpret_cast<const f32x4*>(bias + 16 + 4 * g);
+    }
     const f32x4 is0 = *reinterpret_cast<const f32x4*>(isc + 4 * g);
     const f32x4 is1 = *reinterpret_cast<const f32x4*>(isc + 16 + 4 * g);
     float x[8], s[8], is[8];
@@ -314,13 +322,24 @@ __global__ __launch_bounds__(kThreads8<NB>, 1) void split_fp8_topk_kernel(Args a
     }
     const float base = (m == -INFINITY) ? 0.f : m;
     bf16x8 pv;
+    if (plain) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float pf = fast_exp2(fmaf(x[r], a.scale_log2, -base));
-      const __bf16 wb = static_cast<__bf16>(pf * s[r]);
-      pv[r] = wb;
-      l += pf;
-      lr += is[r] != 0.f ? static_cast<float>(wb) * is[r] : pf;
+      for (int r = 0; r < 8; ++r) {
+        const float pf = fast_exp2(fmaf(x[r], a.scale_log2, -base));
+        const __bf16 wb = static_cast<__bf16>(pf * s[r]);
+        pv[r] = wb;
+        l += pf;
+        lr += static_cast<float>(wb) * is[r];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float pf = fast_exp2(fmaf(x[r], a.scale_log2, -base));
+        const __bf16 wb = static_cast<__bf16>(pf * s[r]);
+        pv[r] = wb;
+        l += pf;
+        lr += is[r] != 0.f ? static_cast<float>(wb) * is[r] : pf;
+      }
     }
 
     // ---- O^T[dim][row] += V^T P^T over this half's 16 column blocks
@@ -373,14 +392,14 @@ __global__ __launch_bounds__(kThreads8<NB>, 1) void split_fp8_topk_kernel(Args a
       lds_barrier();  // staged rows visible to every wave
       if constexpr (kLoad) {
         load_tile<NLW>(regs, ltid, slots_lds, cb, cb, ce, lat, rope, a.kscale, zero_row);
-        store_tile<NLW>(regs, ltid, kv, sc_lds[0][0], sc_lds[0][1], sc_lds[0][2]);
+        store_tile<NLW>(regs, ltid, kv, sc_lds[0][0], sc_lds[0][1], sc_lds[0][2], &plain_lds[0]);
         if (cb + kTile < ce) load_tile<NLW>(regs, ltid, slots_lds, cb, cb + kTile, ce, lat, rope, a.kscale, zero_row);
       }
       lds_barrier();
       int buf = 0;
       for (int t0 = cb; t0 < ce; t0 += kTile) {
         if constexpr (kCompute) {
-          compute_tile(kv + buf * kTileElems, sc_lds[buf][0], sc_lds[buf][1], sc_lds[buf][2]);
+          compute_tile(kv + buf * kTileElems, sc_lds[buf][0], sc_lds[buf][1], sc_lds[buf][2], plain_lds[buf] != 0);
           ++seq;
         }
         if constexpr (kLoad) {
@@ -388,7 +407,7 @@ __global__ __launch_bounds__(kThreads8<NB>, 1) void split_fp8_topk_kernel(Args a
             // The other buffer was last read in the previous tile, which every
             // wave finished before the barrier that ended it.
             store_tile<NLW>(regs, ltid, kv + (buf ^ 1) * kTileElems, sc_lds[buf ^ 1][0], sc_lds[buf ^ 1][1],
-                            sc_lds[buf ^ 1][2]);
+                            sc_lds[buf ^ 1][2], &plain_lds[buf ^ 1]);
             if (t0 + 2 * kTile < ce)
               load_tile<NLW>(regs, ltid, slots_lds, cb, t0 + 2 * kTile, ce, lat, rope, a.kscale, zero_row);
           }
