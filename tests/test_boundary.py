@@ -37,6 +37,33 @@ def test_every_declared_symbol_is_exported(L):
     assert B.abi_version() == 4
 
 
+def test_header_compiles_as_c_and_links(L, tmp_path):
+    # a plain C99 consumer of the boundary: the header parses as C, the
+    # library links, and mla_plan answers as it does through ctypes
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "c_consumer")
+    libdir = os.path.dirname(B.LIB_PATH)
+    cmd = [cc, "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "c_consumer.c"), "-o", exe, "-L", libdir, "-lmla_verify",
+           "-Wl,-rpath," + libdir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    first, second = r.stdout.strip().splitlines()[:2]
+    st, abi, nsplit, blocks, groups, waves, ws = (int(x) for x in first.split())
+    p = B.plan(1, 9, 8, 65545, nsplit=0)
+    assert (st, abi) == (0, 4)
+    assert (nsplit, blocks, groups, waves, ws) == (p["nsplit"], p["row_blocks"], p["row_groups"],
+                                                   p["waves_per_group"], p["workspace_bytes"])
+    assert second == B.lib().mla_status_string(-2).decode()
+
+
 def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert B.status_string(code) and B.status_string(code) != "unknown status"
