@@ -46,11 +46,10 @@ def test_header_compiles_as_c_and_links(L, tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     exe = str(tmp_path / "c_consumer")
-    libdir = os.path.dirname(B.LIB_PATH)
+    # linked by path, so a library selected with MLA_VERIFY_LIB is the one tested
     cmd = [cc, "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
-           os.path.join(ROOT, "tests", "c_consumer.c"), "-o", exe, "-L", libdir, "-lmla_verify",
-           "-Wl,-rpath," + libdir]
+           os.path.join(ROOT, "tests", "c_consumer.c"), "-o", exe, os.path.abspath(B.LIB_PATH)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
