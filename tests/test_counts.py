@@ -43,3 +43,17 @@ def test_bench_table_fixture_consistent():
         naive, flash, sp = float(r[3]), float(r[4]), float(r[5])
         if sp == sp:
             assert abs(naive / flash - sp) < 0.06
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the path runs on one GPU: any other count exits at once with a message
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "8"})):
+        e = dict(os.environ, **env)
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + argv,
+                           capture_output=True, text=True, timeout=60, env=e)
+        assert r.returncode == 2, r.stderr
+        assert "one GPU only" in r.stderr
+        assert r.stdout == ""
