@@ -188,8 +188,14 @@ int release_workspace(int dev, hipStream_t stream) {
 // constants kept, gives 1.52 us, but then 64k prefixes would take 4 blocks,
 // which measured 2-3% slower there than 6; 1.60 keeps the measured order at
 // 16k and 32k, where 4 blocks are fastest, and at 64k.)
-constexpr double kTileUs[7] = {0.0, 1.86, 1.86, 1.86, 1.60, 1.86, 2.21};  // by blocks per workgroup
-constexpr double kFixedUs[7] = {0.0, 8.1, 8.1, 8.1, 8.1, 8.1, 11.4};
+// Groups of 2 and 3 blocks (balanced by their gather-only wavefronts) were
+// fitted on a sweep of H=64 calls (prefixes 256 to 32k, every group size
+// from 2 to 6 at three split counts each): relative to 4 blocks their tile
+// costs 0.76x and 0.95x and their call about 0.9 and 0.2 us less fixed time,
+// scaled onto the constants above. With them, 18 groups of 2 blocks (fewer
+// splits, so fewer partials) win up to 4k positions, as measured.
+constexpr double kTileUs[7] = {0.0, 1.86, 1.21, 1.52, 1.60, 1.86, 2.21};  // by blocks per workgroup
+constexpr double kFixedUs[7] = {0.0, 8.1, 7.2, 7.94, 8.1, 8.1, 11.4};
 constexpr double kPartUsPerByte = 0.49e-6;
 constexpr double kMergeUs = 4.0;
 constexpr int kMaxBlocks = 6;
@@ -324,8 +330,8 @@ Layout plan_layout(int batch, int q_len, int heads, int keys, int kv_dtype, int 
   double best = 0.0;
   bool have = false;
   for (int nb = 1; nb <= kMaxBlocks; ++nb) {
-    // one workgroup when the blocks fit; otherwise 4 to 6 blocks per group
-    if (blocks <= kMaxBlocks ? nb != blocks : nb < 4) continue;
+    // one workgroup when the blocks fit; otherwise 2 to 6 blocks per group
+    if (blocks <= kMaxBlocks ? nb != blocks : nb < 2) continue;
 #ifdef MLA_ONLY_NB
     if (blocks > kMaxBlocks && nb != MLA_ONLY_NB) continue;  // tuning builds that time one group size
 #endif

@@ -171,11 +171,15 @@ def test_choose_nsplit_rules(L):
     # an explicit split count keeps one pass of the grid for the smaller groups
     assert B.plan(1, 9, 8, 16393, nsplit=129)["row_groups"] == 1
     assert B.plan(1, 9, 8, 16393, nsplit=128)["row_groups"] == 2
-    # H=64 short: 9 row groups of 4 blocks, at most 28 splits (252
-    # workgroups, one wave); 129 tiles need 5 per split, which 26 splits give
-    assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 26
+    # H=64 short: 18 row groups of 2 blocks, at most 14 splits (252
+    # workgroups, one wave); 129 tiles need 10 per split, which 13 splits
+    # give. Fewer splits than 9 groups of 4 (26) means fewer partials: split +
+    # merge measured 24.6 against 27.5 us
+    assert B.choose_nsplit(1, 9, 64, 4105, num_cus=256) == 13
     p = B.plan(1, 9, 64, 4105)
-    assert (p["row_blocks"], p["row_groups"], p["grid"]) == (4, 9, 234)
+    assert (p["row_blocks"], p["row_groups"], p["grid"], p["waves_per_group"]) == (2, 18, 234, 8)
+    # from 8k positions the larger groups win again (fewer key reads per row)
+    assert B.plan(1, 9, 64, 8201)["row_blocks"] == 4
     # H=64 at 16k: 9 row groups of 4 blocks (each with four gather-only
     # wavefronts) and 27 splits, 19 tiles each; 8 groups of 5 would give 17
     # tiles but a dearer tile (measured 43.7 against 46.2 us of kernel time)
@@ -210,12 +214,14 @@ def test_plan_shapes(L):
     assert p["workspace_bytes"] == 64 * 72 * 1036 + 4
     p = B.plan(1, 9, 8, 16393, nsplit=200)
     assert (p["nsplit"], p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (200, 12, 1, 200, 5)
+    # 16 splits: 18 groups of 2 would need 288 workgroups (two passes), so
+    # 12 groups of 3 (192, one pass)
     p = B.plan(1, 9, 64, 4105, nsplit=16)
-    assert (p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (12, 9, 144, 4)
-    # 144 rows = 9 blocks: one pass of the grid either way, so 3 groups of 4
-    # (the smaller workgroups start and finish sooner)
+    assert (p["waves_per_group"], p["row_groups"], p["grid"], p["row_blocks"]) == (8, 12, 192, 3)
+    # 144 rows = 9 blocks: one pass of the grid with any group size, so 5
+    # groups of 2 (the cheapest tile)
     p = B.plan(1, 9, 16, 4105, nsplit=16)
-    assert (p["waves_per_group"], p["row_groups"], p["row_blocks"]) == (12, 3, 4)
+    assert (p["waves_per_group"], p["row_groups"], p["row_blocks"]) == (8, 5, 2)
     p = B.plan(2, 1, 1, 10, nsplit=1)
     assert p["workspace_bytes"] == 0 and p["waves_per_group"] == 4
 

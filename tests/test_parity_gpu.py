@@ -41,8 +41,8 @@ def test_c1_small_verify():
 
 
 def test_c2_full_heads():
-    # 8, 16 and the library's 26 splits run 9 row groups of 4 blocks; 32 and
-    # 64 run 8 groups of 5, the last with one live block
+    # 8 splits and the library's 13 run 18 row groups of 2 blocks, 16 run 12
+    # groups of 3, 32 and 64 run 8 groups of 5 (the last with one live block)
     _check(I.workload("c2"), [8, 16, 32, 64, 0])
 
 
