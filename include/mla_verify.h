@@ -211,13 +211,14 @@ int mla_plan(const mla_q_t* q, const mla_kv_t* kv_cache, const mla_mask_t* mask_
  * deterministic and safe under graph capture. At most one split-kernel
  * workgroup per CU. For a bf16 cache the library picks the query rows per
  * workgroup (up to six 16-row blocks; more rows are dealt to several
- * workgroups that gather the same keys) together with the count s, by a
- * cost model fitted to cold-cache calls on MI355X: about 1.86 us per
- * 32-position tile of the slowest split (2.21 us with six blocks per
- * workgroup), 8 us fixed (11.4 us with six blocks), and, when s > 1, 4 us
- * for the merge plus 0.49 us per MB of partials (1036 bytes per split and
- * query row, written and read back); the cheapest wins, the fewest splits on
- * ties. A single sequence whose rows fill exactly five blocks (e.g. 8 heads,
+ * workgroups of two to six blocks that gather the same keys) together with
+ * the count s, by a cost model fitted to cold-cache calls on MI355X: per
+ * 32-position tile of the slowest split about 1.21, 1.52, 1.60, 1.86 and
+ * 2.21 us with two, three, four, five and six blocks per workgroup (1.86 us
+ * with one), 7.2 to 8.1 us fixed (11.4 us with six blocks), and, when
+ * s > 1, 4 us for the merge plus 0.49 us per MB of partials (1036 bytes per
+ * split and query row, written and read back); the cheapest wins, the
+ * fewest splits on ties. A single sequence whose rows fill exactly five blocks (e.g. 8 heads,
  * q_len 9) may instead be dealt to two groups of three blocks or three of
  * two, chosen with the count by split + merge times fitted per layout (the
  * smaller groups win below about 32k positions: fewer wavefronts per SIMD
